@@ -1,0 +1,246 @@
+"""Python binding of libhga (HGA routed attention on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libhga.so,
+called through its C ABI (include/hga.h). PyTorch supplies device memory and
+the current stream. There is no fallback: if the library is missing this
+module raises at import time.
+
+    cm, gm = build_summaries(K, chunk, group)
+    chunk_idx, group_idx = route(Q, cm, gm, T, chunk, group, k_chunk, k_group)
+    O, lse = attend(Q, K, V, group_idx, group)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summaries",
+           "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
+           "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
+
+F32, BF16 = 0, 1
+_STATUS = {0: "HGA_OK", -1: "HGA_ERR_NULL", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_DTYPE",
+           -4: "HGA_ERR_LAYOUT", -5: "HGA_ERR_PARAM", -6: "HGA_ERR_WORKSPACE",
+           -7: "HGA_ERR_HIP", -8: "HGA_ERR_UNSUPPORTED"}
+
+
+class HGAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = _lib.hga_status_str(status).decode() if _lib is not None else ""
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({text})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("q_heads", ctypes.c_int64),
+                ("kv_heads", ctypes.c_int64), ("n_queries", ctypes.c_int64),
+                ("seq_len", ctypes.c_int64), ("head_dim", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libhga.so not built at {LIB_PATH}; run "
+                          "`python -m hierarchical_sparse_attention_summaries_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    P = ctypes.POINTER
+    sig = {
+        "hga_abi_version": (ctypes.c_int, []),
+        "hga_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "hga_summary_counts": (ctypes.c_int, [i64, i32, i32, P(i64), P(i64)]),
+        "hga_build_summaries": (ctypes.c_int, [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp]),
+        "hga_update_summaries": (ctypes.c_int, [vp, i32, i64, i64, i64, i64, i32, i32, i64, i64,
+                                                vp, vp, vp]),
+        "hga_route_workspace_size": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, P(sz)]),
+        "hga_route": (ctypes.c_int, [P(Shape), vp, i32, vp, vp, i32, i32, i32, i32, f32, vp, vp,
+                                     vp, sz, vp]),
+        "hga_attend_workspace_size": (ctypes.c_int, [P(Shape), i32, i32, P(sz)]),
+        "hga_attend": (ctypes.c_int, [P(Shape), vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, vp,
+                                      sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise HGAError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, host_ok: bool = False):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be on a GPU" + (" or pinned host memory" if host_ok else ""))
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+# Zero-initialised workspaces, one per (device, role), grown on demand. The
+# library leaves their counters at zero after each call.
+_ws_lock = threading.Lock()
+_ws: dict = {}
+
+
+def _workspace(device: torch.device, role: str, nbytes: int) -> torch.Tensor:
+    key = (device.index, role)
+    with _ws_lock:
+        buf = _ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _ws[key] = buf
+        return buf
+
+
+def summary_counts(seq_len: int, chunk: int, group: int):
+    nc, ng = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.hga_summary_counts(seq_len, chunk, group, ctypes.byref(nc), ctypes.byref(ng)),
+           "hga_summary_counts")
+    return nc.value, ng.value
+
+
+def build_summaries(K: torch.Tensor, chunk: int, group: int, chunk_mean=None, group_mean=None):
+    """Mean key per chunk and per group. K [B, Hkv, T, D] -> ([B,Hkv,n_c,D], [B,Hkv,n_g,D]) f32."""
+    _need(K, "K", 4)
+    B, H, T, D = K.shape
+    n_c, n_g = summary_counts(T, chunk, group)
+    if chunk_mean is None:
+        chunk_mean = torch.empty((B, H, n_c, D), dtype=torch.float32, device=K.device)
+    if group_mean is None:
+        group_mean = torch.empty((B, H, n_g, D), dtype=torch.float32, device=K.device)
+    _need(chunk_mean, "chunk_mean", 4)
+    _need(group_mean, "group_mean", 4)
+    if tuple(chunk_mean.shape) != (B, H, n_c, D) or tuple(group_mean.shape) != (B, H, n_g, D) \
+            or chunk_mean.dtype != torch.float32 or group_mean.dtype != torch.float32:
+        raise ValueError("summary buffers must be float32 [B, Hkv, n, D]")
+    _check(_lib.hga_build_summaries(_ptr(K), _dtype_code(K), B, H, T, D, chunk, group,
+                                    _ptr(chunk_mean), _ptr(group_mean), _stream(K.device)),
+           "hga_build_summaries")
+    return chunk_mean, group_mean
+
+
+def update_summaries(K: torch.Tensor, chunk: int, group: int, t_begin: int, t_end: int,
+                     chunk_mean: torch.Tensor, group_mean: torch.Tensor):
+    """Recompute the summaries of the chunks (and their groups) touching [t_begin, t_end)."""
+    _need(K, "K", 4)
+    _need(chunk_mean, "chunk_mean", 4)
+    _need(group_mean, "group_mean", 4)
+    B, H, T, D = K.shape
+    n_c, n_g = summary_counts(T, chunk, group)
+    if tuple(chunk_mean.shape) != (B, H, n_c, D) or tuple(group_mean.shape) != (B, H, n_g, D):
+        raise ValueError("summary buffers do not match K")
+    _check(_lib.hga_update_summaries(_ptr(K), _dtype_code(K), B, H, T, D, chunk, group, t_begin,
+                                     t_end, _ptr(chunk_mean), _ptr(group_mean), _stream(K.device)),
+           "hga_update_summaries")
+
+
+def _shape(Q: torch.Tensor, Hkv: int, T: int) -> Shape:
+    B, Hq, Nq, D = Q.shape
+    return Shape(B, Hq, Hkv, Nq, T, D)
+
+
+def route_workspace_bytes(shape: Shape, chunk, group, k_chunk, k_group) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.hga_route_workspace_size(ctypes.byref(shape), chunk, group, k_chunk, k_group,
+                                         ctypes.byref(n)), "hga_route_workspace_size")
+    return n.value
+
+
+def attend_workspace_bytes(shape: Shape, group, k_group) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.hga_attend_workspace_size(ctypes.byref(shape), group, k_group, ctypes.byref(n)),
+           "hga_attend_workspace_size")
+    return n.value
+
+
+def route(Q: torch.Tensor, chunk_mean: torch.Tensor, group_mean: torch.Tensor, seq_len: int,
+          chunk: int, group: int, k_chunk: int, k_group: int, scale: float = 0.0,
+          want_chunks: bool = True, chunk_idx=None, group_idx=None, workspace=None):
+    """Two-level routing. Returns (chunk_idx [B,Hq,Nq,k_chunk+2] or None, group_idx [B,Hq,Nq,k_group])."""
+    _need(Q, "Q", 4)
+    _need(chunk_mean, "chunk_mean", 4)
+    _need(group_mean, "group_mean", 4)
+    B, Hq, Nq, D = Q.shape
+    Hkv = chunk_mean.shape[1]
+    n_c, n_g = summary_counts(seq_len, chunk, group)
+    if tuple(chunk_mean.shape) != (B, Hkv, n_c, D) or tuple(group_mean.shape) != (B, Hkv, n_g, D):
+        raise ValueError("summary shapes do not match Q / seq_len")
+    shape = _shape(Q, Hkv, seq_len)
+    nbytes = route_workspace_bytes(shape, chunk, group, k_chunk, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "route", nbytes)
+    if want_chunks and chunk_idx is None:
+        chunk_idx = torch.empty((B, Hq, Nq, k_chunk + 2), dtype=torch.int32, device=Q.device)
+    if group_idx is None:
+        group_idx = torch.empty((B, Hq, Nq, k_group), dtype=torch.int32, device=Q.device)
+    _check(_lib.hga_route(ctypes.byref(shape), _ptr(Q), _dtype_code(Q), _ptr(chunk_mean),
+                          _ptr(group_mean), chunk, group, k_chunk, k_group, float(scale),
+                          _ptr(chunk_idx), _ptr(group_idx), _ptr(ws), ws.numel(),
+                          _stream(Q.device)), "hga_route")
+    return chunk_idx, group_idx
+
+
+def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, group_idx: torch.Tensor, group: int,
+           scale: float = 0.0, want_lse: bool = True, out=None, lse=None, workspace=None):
+    """Exact attention over the routed groups. Returns (O like Q, lse [B,Hq,Nq] f32 or None).
+    K and V may be pinned host tensors (read in place over the host link)."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    _need(V, "V", 4, host_ok=True)
+    _need(group_idx, "group_idx", 4)
+    if group_idx.dtype != torch.int32:
+        raise TypeError("group_idx must be int32")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share one dtype")
+    B, Hq, Nq, D = Q.shape
+    Hkv, T = K.shape[1], K.shape[2]
+    if tuple(K.shape) != (B, Hkv, T, D) or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K/V shapes do not match Q")
+    k_group = group_idx.shape[3]
+    if tuple(group_idx.shape[:3]) != (B, Hq, Nq):
+        raise ValueError("group_idx must be [B, Hq, Nq, k_group]")
+    shape = _shape(Q, Hkv, T)
+    nbytes = attend_workspace_bytes(shape, group, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "attend", nbytes)
+    if out is None:
+        out = torch.empty_like(Q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    _check(_lib.hga_attend(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q),
+                           _ptr(group_idx), k_group, group, float(scale), _ptr(out),
+                           _ptr(lse if want_lse else None), _ptr(ws), ws.numel(),
+                           _stream(Q.device)), "hga_attend")
+    return out, (lse if want_lse else None)

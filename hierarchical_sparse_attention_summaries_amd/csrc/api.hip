@@ -1,0 +1,242 @@
+// C ABI of libhga (declared in include/hga.h): argument checks on the host,
+// then stream-ordered launches. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/hga.h"
+#include "hga_internal.h"
+
+namespace hga {
+
+int device_cu_count() {
+  // Launch shapes are planned for MI355X/MI350X (gfx950): 256 CUs in 8 XCDs.
+  // Planning never queries the device, so size queries work without one.
+  return 256;
+}
+
+}  // namespace hga
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dtype_ok(int32_t dtype) { return dtype == HGA_F32 || dtype == HGA_BF16; }
+
+int check_chunking(int64_t T, int32_t chunk, int32_t group) {
+  if (chunk < 1 || group < 1 || chunk % group != 0) return HGA_ERR_PARAM;
+  if (group > 65536 || chunk / group > 4096) return HGA_ERR_PARAM;
+  if (T < 1 || T >= kMaxDim) return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
+
+int check_shape(const hga_shape* s) {
+  if (!s) return HGA_ERR_NULL;
+  if (s->batch < 1 || s->q_heads < 1 || s->kv_heads < 1 || s->n_queries < 1 || s->seq_len < 1)
+    return HGA_ERR_SHAPE;
+  if (s->q_heads % s->kv_heads != 0) return HGA_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_SHAPE;
+  if (s->n_queries > s->seq_len) return HGA_ERR_SHAPE;
+  const int64_t rows = s->batch * s->q_heads * s->n_queries;
+  if (s->batch >= kMaxDim || s->q_heads >= kMaxDim || s->seq_len >= kMaxDim || rows >= kMaxDim ||
+      s->batch * s->kv_heads * s->seq_len >= (int64_t(1) << 40))
+    return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
+
+int check_route_params(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
+                       int32_t k_group) {
+  int st = check_chunking(s->seq_len, chunk, group);
+  if (st != HGA_OK) return st;
+  if (k_chunk < 0 || k_group < 1) return HGA_ERR_PARAM;
+  const int64_t n_c = (s->seq_len + chunk - 1) / chunk;
+  const int64_t gpc = chunk / group;
+  const int64_t n_g = (s->seq_len + group - 1) / group;
+  const int64_t kept = std::min<int64_t>(int64_t(k_chunk) + 2, n_c);
+  if (n_c - 2 > hga::kMaxSelectItems || kept * gpc > hga::kMaxSelectItems)
+    return HGA_ERR_UNSUPPORTED;
+  if (s->batch * s->q_heads * s->n_queries * (n_c + n_g) >= (int64_t(1) << 40))
+    return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int hga_abi_version(void) { return HGA_ABI_VERSION; }
+
+const char* hga_status_str(int status) {
+  switch (status) {
+    case HGA_OK: return "ok";
+    case HGA_ERR_NULL: return "a required pointer is NULL";
+    case HGA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case HGA_ERR_DTYPE: return "unknown dtype";
+    case HGA_ERR_LAYOUT: return "a pointer is not 16-byte aligned";
+    case HGA_ERR_PARAM: return "chunk/group/k_chunk/k_group/range out of range";
+    case HGA_ERR_WORKSPACE: return "workspace too small";
+    case HGA_ERR_HIP: return "HIP call or kernel launch failed";
+    case HGA_ERR_UNSUPPORTED: return "request not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int hga_summary_counts(int64_t seq_len, int32_t chunk, int32_t group, int64_t* n_chunks,
+                       int64_t* n_groups) {
+  const int st = check_chunking(seq_len, chunk, group);
+  if (st != HGA_OK) return st;
+  if (n_chunks) *n_chunks = (seq_len + chunk - 1) / chunk;
+  if (n_groups) *n_groups = (seq_len + group - 1) / group;
+  return HGA_OK;
+}
+
+static int summaries_common(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
+                            int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
+                            int64_t t_begin, int64_t t_end, float* chunk_mean,
+                            float* group_mean, void* stream) {
+  if (!K || !chunk_mean || !group_mean) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  if (batch < 1 || kv_heads < 1 || batch >= kMaxDim || kv_heads >= kMaxDim) return HGA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return HGA_ERR_SHAPE;
+  int st = check_chunking(seq_len, chunk, group);
+  if (st != HGA_OK) return st;
+  if (batch * kv_heads * seq_len >= (int64_t(1) << 40)) return HGA_ERR_SHAPE;
+  if (t_begin < 0 || t_end > seq_len || t_begin >= t_end) return HGA_ERR_PARAM;
+  if (!aligned16(K) || !aligned16(chunk_mean) || !aligned16(group_mean)) return HGA_ERR_LAYOUT;
+  const int64_t c_begin = t_begin / chunk;
+  const int64_t c_end = (t_end + chunk - 1) / chunk;
+  if (batch * kv_heads * (c_end - c_begin) >= kMaxDim) return HGA_ERR_SHAPE;
+  const hipError_t e = hga::launch_summaries(K, dtype, batch * kv_heads, head_dim, seq_len, chunk,
+                                             group, static_cast<int>(c_begin),
+                                             static_cast<int>(c_end), chunk_mean, group_mean,
+                                             as_stream(stream));
+  return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
+}
+
+int hga_build_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
+                        int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
+                        float* chunk_mean, float* group_mean, void* stream) {
+  return summaries_common(K, dtype, batch, kv_heads, seq_len, head_dim, chunk, group, 0, seq_len,
+                          chunk_mean, group_mean, stream);
+}
+
+int hga_update_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
+                         int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
+                         int64_t t_begin, int64_t t_end, float* chunk_mean, float* group_mean,
+                         void* stream) {
+  return summaries_common(K, dtype, batch, kv_heads, seq_len, head_dim, chunk, group, t_begin,
+                          t_end, chunk_mean, group_mean, stream);
+}
+
+int hga_route_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
+                             int32_t k_chunk, int32_t k_group, size_t* bytes) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  *bytes = hga::plan_route(shape->batch, shape->q_heads, shape->kv_heads, shape->n_queries,
+                           shape->seq_len, chunk, group, k_chunk, k_group)
+               .bytes;
+  return HGA_OK;
+}
+
+int hga_route(const hga_shape* shape, const void* Q, int32_t dtype, const float* chunk_mean,
+              const float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+              int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !chunk_mean || !group_mean || !group_idx || !workspace) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  if (!aligned16(Q) || !aligned16(chunk_mean) || !aligned16(group_mean) || !aligned16(workspace))
+    return HGA_ERR_LAYOUT;
+  const hga::RoutePlan plan = hga::plan_route(shape->batch, shape->q_heads, shape->kv_heads,
+                                              shape->n_queries, shape->seq_len, chunk, group,
+                                              k_chunk, k_group);
+  if (workspace_bytes < plan.bytes) return HGA_ERR_WORKSPACE;
+  hga::RouteArgs a{};
+  a.Q = Q;
+  a.chunk_mean = chunk_mean;
+  a.group_mean = group_mean;
+  a.B = static_cast<int>(shape->batch);
+  a.Hq = static_cast<int>(shape->q_heads);
+  a.Hkv = static_cast<int>(shape->kv_heads);
+  a.Nq = static_cast<int>(shape->n_queries);
+  a.T = static_cast<int>(shape->seq_len);
+  a.D = static_cast<int>(shape->head_dim);
+  a.C = chunk;
+  a.G = group;
+  a.gpc = chunk / group;
+  a.n_c = static_cast<int>((shape->seq_len + chunk - 1) / chunk);
+  a.n_g = static_cast<int>((shape->seq_len + group - 1) / group);
+  a.k_c = k_chunk;
+  a.k_g = k_group;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(shape->head_dim));
+  a.chunk_idx = chunk_idx;
+  a.group_idx = group_idx;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
+  a.chunk_scores = reinterpret_cast<float*>(ws + plan.off_chunk_scores);
+  a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
+  const hipError_t e = hga::launch_route(a, dtype, plan, as_stream(stream));
+  return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
+}
+
+int hga_attend_workspace_size(const hga_shape* shape, int32_t group, int32_t k_group,
+                              size_t* bytes) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  if (group < 1 || group > 65536 || k_group < 1) return HGA_ERR_PARAM;
+  const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
+  *bytes = hga::plan_attend(rows, shape->head_dim, group, k_group).bytes;
+  return HGA_OK;
+}
+
+int hga_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
+               int32_t dtype, const int32_t* group_idx, int32_t k_group, int32_t group,
+               float scale, void* O, float* lse, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !group_idx || !O || !workspace) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  if (group < 1 || group > 65536 || k_group < 1) return HGA_ERR_PARAM;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+    return HGA_ERR_LAYOUT;
+  const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
+  const hga::AttendPlan plan = hga::plan_attend(rows, shape->head_dim, group, k_group);
+  if (workspace_bytes < plan.bytes) return HGA_ERR_WORKSPACE;
+  if (rows * plan.n_splits >= kMaxDim) return HGA_ERR_SHAPE;
+  hga::AttendArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.group_idx = group_idx;
+  a.O = O;
+  a.lse = lse;
+  a.B = static_cast<int>(shape->batch);
+  a.Hq = static_cast<int>(shape->q_heads);
+  a.Hkv = static_cast<int>(shape->kv_heads);
+  a.Nq = static_cast<int>(shape->n_queries);
+  a.T = static_cast<int>(shape->seq_len);
+  a.D = static_cast<int>(shape->head_dim);
+  a.G = group;
+  a.k_g = k_group;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(shape->head_dim));
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
+  a.partials = reinterpret_cast<float*>(ws + plan.off_partials);
+  const hipError_t e = hga::launch_attend(a, dtype, plan, as_stream(stream));
+  return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
+}
+
+}  // extern "C"

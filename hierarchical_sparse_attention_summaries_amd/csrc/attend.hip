@@ -1,0 +1,229 @@
+// Step 3 of HGA (abstract of "Hierarchical Global Attention (HGA)", arXiv
+// 2606.30709): exact token-level softmax attention over the routed tokens only.
+//
+// Each query row (b, h, i) owns k_group routed groups. A wave takes
+// `groups_per_wave` of them; for each group it gathers the group's keys and
+// values straight from HBM (a group is G contiguous rows of K and of V, read
+// with 16-byte coalesced loads, all loads of a 32-token tile issued before any
+// use) and folds them into an online softmax (running max m, sum l and output
+// o in fp32, exponentials in base 2 with log2(e) folded into the query). The
+// four waves of a workgroup merge in LDS; the workgroups of a row (split-K over
+// its groups) leave (m, l, o) partials and the last one to arrive merges them
+// and writes O and lse. HBM-bound: every routed K/V byte is read once.
+#include <math.h>
+
+#include "hga_device.h"
+#include "hga_internal.h"
+
+namespace hga {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTile = 32;  // tokens per gather tile
+
+template <typename TKV, int D>
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
+                                                          int n_splits) {
+  constexpr int EPL = Elem<TKV>::kPer16;
+  constexpr int LPR = D / EPL;        // lanes per token row
+  constexpr int RPL = kWave / LPR;    // token rows per wave-wide load
+  constexpr int NLD = kTile / RPL;    // loads per tile (per K and per V)
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+
+  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float s_o[kWaves][D];
+  __shared__ bool s_last;
+
+  const int row = blockIdx.x / n_splits;
+  const int split = blockIdx.x % n_splits;
+  const int i = row % a.Nq;
+  const int bh = row / a.Nq;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int kv = h / (a.Hq / a.Hkv);
+  const int p = a.T - a.Nq + i;
+  const int t_lim = p + 1;  // tokens j <= p (and j < T since p < T)
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int sub = lane / LPR;
+  const int col = (lane % LPR) * EPL;
+
+  const TKV* Kb = static_cast<const TKV*>(a.K) + static_cast<size_t>(b * a.Hkv + kv) * a.T * D;
+  const TKV* Vb = static_cast<const TKV*>(a.V) + static_cast<size_t>(b * a.Hkv + kv) * a.T * D;
+
+  float q[EPL];
+  {
+    widen(ld16(static_cast<const TKV*>(a.Q) + static_cast<size_t>(row) * D + col), q);
+    const float s = a.scale * kLog2e;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) q[e] *= s;
+  }
+
+  float m = -INFINITY, l = 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+
+  const int32_t* gl = a.group_idx + static_cast<size_t>(row) * a.k_g;
+  const int e0 = (split * kWaves + wave) * groups_per_wave;
+  const int e1 = min(e0 + groups_per_wave, a.k_g);
+  const int n_g = (a.T + a.G - 1) / a.G;
+  for (int e = e0; e < e1; ++e) {
+    const int g = gl[e];
+    if (g < 0 || g >= n_g) continue;  // -1 padding (and ids out of range) carry no tokens
+    const int t0 = g * a.G;
+    const int t1 = min(t0 + a.G, t_lim);
+    for (int base = t0; base < t1; base += kTile) {
+      uint4 kr[NLD], vr[NLD];
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int t = base + u * RPL + sub;
+        if (t < t1) {
+          kr[u] = ld16(Kb + static_cast<size_t>(t) * D + col);
+          vr[u] = ld16(Vb + static_cast<size_t>(t) * D + col);
+        } else {
+          kr[u] = make_uint4(0, 0, 0, 0);
+          vr[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      float s[NLD];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        float x[EPL];
+        widen(kr[u], x);
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) d = fmaf(q[k], x[k], d);
+        d = group_sum<LPR>(d);
+        s[u] = (base + u * RPL + sub < t1) ? d : -INFINITY;
+        mt = fmaxf(mt, s[u]);
+      }
+      mt = across_rows_max<LPR>(mt);
+      const float m_new = fmaxf(m, mt);  // finite: token `base` is always valid
+      const float corr = exp2f(m - m_new);
+      l *= corr;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) o[k] *= corr;
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const float pu = exp2f(s[u] - m_new);
+        l += pu;
+        float x[EPL];
+        widen(vr[u], x);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) o[k] = fmaf(pu, x[k], o[k]);
+      }
+      m = m_new;
+    }
+  }
+  // Lanes of one column slot hold disjoint token rows: fold them.
+  l = across_rows_sum<LPR>(l);
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) o[k] = across_rows_sum<LPR>(o[k]);
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) s_o[wave][col + k] = o[k];
+  }
+  __syncthreads();
+
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w]);
+  float Lsum = 0.f, acc = 0.f;
+  const int d = threadIdx.x;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2f(s_m[w] - M);
+      Lsum += s_l[w] * f;
+      if (d < D) acc += s_o[w][d] * f;
+    }
+  }
+
+  auto finish = [&](float Mx, float Lx, float ox) {
+    if (d < D) {
+      const float v = Lx > 0.f ? ox / Lx : 0.f;
+      const size_t off = static_cast<size_t>(row) * D + d;
+      if constexpr (sizeof(TKV) == 4) {
+        static_cast<float*>(a.O)[off] = v;
+      } else {
+        static_cast<uint16_t*>(a.O)[off] = static_cast<uint16_t>(bf16_bits(v));
+      }
+    }
+    if (a.lse && d == 0) a.lse[row] = Lx > 0.f ? (Mx + log2f(Lx)) * kLn2 : -INFINITY;
+  };
+
+  if (n_splits == 1) {
+    finish(M, Lsum, acc);
+    return;
+  }
+  float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
+  if (d < D) part[2 + d] = acc;
+  if (d == 0) {
+    part[0] = M;
+    part[1] = Lsum;
+  }
+  if (!arrive_last(a.counters + row, static_cast<unsigned>(n_splits), &s_last)) return;
+
+  const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
+  float Mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, rp[s * (D + 2)]);
+  float Lx = 0.f, ox = 0.f;
+  if (Mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ms = rp[s * (D + 2)];
+      const float f = exp2f(ms - Mx);
+      Lx += rp[s * (D + 2) + 1] * f;
+      if (d < D) ox += rp[s * (D + 2) + 2 + d] * f;
+    }
+  }
+  finish(Mx, Lx, ox);
+}
+
+template <typename TKV, int D>
+hipError_t launch_t(const AttendArgs& a, const AttendPlan& plan, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.Nq;
+  const unsigned blocks = static_cast<unsigned>(rows * plan.n_splits);
+  hipLaunchKernelGGL((attend_kernel<TKV, D>), dim3(blocks), dim3(kThreads), 0, stream, a,
+                     plan.groups_per_wave, plan.n_splits);
+  return hipGetLastError();
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g) {
+  AttendPlan pl{};
+  // Enough waves to keep every CU's memory pipe busy (>= 16 waves per CU), no
+  // more: larger groups_per_wave means fewer partials to merge.
+  const int64_t target_waves = 16 * static_cast<int64_t>(device_cu_count());
+  int gpw = 1;
+  while (gpw < 16 && rows * ((k_g + 2 * gpw - 1) / (2 * gpw)) >= target_waves) gpw *= 2;
+  (void)G;
+  pl.groups_per_wave = gpw;
+  const int waves_per_row = (k_g + gpw - 1) / gpw;
+  pl.n_splits = (waves_per_row + kWaves - 1) / kWaves;
+  pl.off_counters = 0;
+  pl.off_partials = align_up(static_cast<size_t>(rows) * sizeof(unsigned), 256);
+  const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;
+  pl.bytes = align_up(pl.off_partials + part, 256);
+  return pl;
+}
+
+hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
+                         hipStream_t stream) {
+  if (dtype == kF32)
+    return a.D == 64 ? launch_t<float, 64>(a, plan, stream) : launch_t<float, 128>(a, plan, stream);
+  return a.D == 64 ? launch_t<uint16_t, 64>(a, plan, stream)
+                   : launch_t<uint16_t, 128>(a, plan, stream);
+}
+
+}  // namespace hga

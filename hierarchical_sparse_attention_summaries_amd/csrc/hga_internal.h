@@ -1,0 +1,73 @@
+// Internal launchers behind the C ABI in include/hga.h. Arguments reaching
+// these functions have been validated by the ABI layer (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hga {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Largest number of items one wave selects from (middle chunks, or candidate
+// groups of the kept chunks).
+constexpr int kMaxSelectItems = 4096;
+
+hipError_t launch_summaries(const void* K, int dtype, int64_t BH, int64_t D, int64_t T,
+                            int C, int G, int c_begin, int c_end, float* chunk_mean,
+                            float* group_mean, hipStream_t stream);
+
+struct RoutePlan {
+  int q_per_block;      // queries of one sequence scored together per KV head
+  int n_qblocks;        // ceil(Nq / q_per_block)
+  int chunks_per_split; // chunks (and their groups) scored per workgroup
+  int n_splits;         // workgroups per (sequence, KV head, query block)
+  size_t off_counters, off_chunk_scores, off_group_scores, bytes;
+};
+RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int C, int G,
+                     int k_c, int k_g);
+
+struct RouteArgs {
+  const void* Q;
+  const float* chunk_mean;
+  const float* group_mean;
+  int B, Hq, Hkv, Nq, T, D;
+  int C, G, gpc, n_c, n_g;
+  int k_c, k_g;
+  float scale;
+  int32_t* chunk_idx;  // may be null
+  int32_t* group_idx;
+  float* chunk_scores; // workspace [B*Hq*Nq, n_c]
+  float* group_scores; // workspace [B*Hq*Nq, n_g]
+  unsigned* counters;  // workspace [B*Hkv*n_qblocks]
+};
+hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hipStream_t stream);
+
+struct AttendPlan {
+  int groups_per_wave;
+  int n_splits;         // workgroups per query row
+  size_t off_counters, off_partials, bytes;
+};
+AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g);
+
+struct AttendArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const int32_t* group_idx;
+  void* O;
+  float* lse;          // may be null
+  int B, Hq, Hkv, Nq, T, D;
+  int G, k_g;
+  float scale;
+  float* partials;     // workspace [rows, n_splits, D + 2]
+  unsigned* counters;  // workspace [rows]
+};
+hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
+                         hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace hga

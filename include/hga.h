@@ -1,0 +1,171 @@
+/*
+ * libhga: Hierarchical Global Attention (HGA) routed attention for AMD MI355X (gfx950).
+ *
+ * The method (abstract of "Hierarchical Global Attention (HGA)", arXiv 2606.30709,
+ * searcharxiv.com page): a drop-in replacement for dense causal attention with the
+ * model's W_Q/W_K/W_V/W_O untouched. For every query head it (1) scores compact
+ * RoPE-aware summaries of key chunks and retrieves the relevant chunks, (2) routes
+ * only the most relevant groups inside those chunks, and (3) runs exact token-level
+ * softmax attention over the retrieved tokens only (about 3% of the context).
+ *
+ * Readings where the abstract is silent, used by every call below:
+ *   - a summary is the mean of the post-RoPE keys of a group or chunk;
+ *   - a score is q . summary * scale (scale = 1/sqrt(D) unless given);
+ *   - the first chunk and the query's own chunk are always kept, in addition to
+ *     the k_chunk best of the other chunks before the query's chunk;
+ *   - the k_group best groups are chosen globally among all groups of the kept
+ *     chunks whose first position is <= p (forced chunks' groups compete too);
+ *   - ties go to the lower index; index lists are ascending and -1 padded;
+ *   - query i of Nq sits at position p = T - Nq + i and attends to j <= p.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major (innermost dimension last, stride 1), and
+ *     live in device memory (or host memory the device can address, see
+ *     hga_attend). The caller owns every buffer; the library allocates no device
+ *     memory and keeps no pointer after a call returns.
+ *   - Query head h reads KV head h / (q_heads / kv_heads).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued in
+ *     stream order; nothing synchronises. Results are ready when the stream is.
+ *   - Every call returns an hga_status. Arguments are checked on the host before
+ *     anything is enqueued; a rejected call enqueues nothing. HGA_ERR_HIP means a
+ *     launch failed; faults inside kernels surface at the caller's next
+ *     synchronisation, as usual for HIP. Nothing throws, prints or aborts.
+ *   - Inputs must be finite (no NaN/Inf in Q, K, V).
+ *   - Workspaces: the first hga_*_workspace_size bytes must be zero-filled before
+ *     their first use (e.g. allocate them zeroed). A call that returns HGA_OK leaves
+ *     the workspace's counters at zero again, so a workspace can be reused
+ *     call after call. Calls that may run concurrently must not share one.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HGA_ABI_VERSION 1
+
+typedef enum hga_status {
+  HGA_OK = 0,
+  HGA_ERR_NULL = -1,        /* a required pointer is NULL */
+  HGA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  HGA_ERR_DTYPE = -3,       /* unknown dtype code */
+  HGA_ERR_LAYOUT = -4,      /* a pointer is not 16-byte aligned */
+  HGA_ERR_PARAM = -5,       /* chunk/group/k_chunk/k_group/range out of range */
+  HGA_ERR_WORKSPACE = -6,   /* workspace smaller than the size query says */
+  HGA_ERR_HIP = -7,         /* a HIP call or kernel launch failed */
+  HGA_ERR_UNSUPPORTED = -8  /* a valid request this build has no kernel for */
+} hga_status;
+
+typedef enum hga_dtype {
+  HGA_F32 = 0,   /* IEEE binary32 */
+  HGA_BF16 = 1   /* bfloat16, stored as 16-bit words */
+} hga_dtype;
+
+/* Sizes of one attention call. */
+typedef struct hga_shape {
+  int64_t batch;      /* B  >= 1 sequences */
+  int64_t q_heads;    /* Hq >= 1 query heads, a multiple of kv_heads */
+  int64_t kv_heads;   /* Hkv >= 1 KV heads */
+  int64_t n_queries;  /* Nq, 1 <= Nq <= T: queries per sequence, at positions T-Nq .. T-1 */
+  int64_t seq_len;    /* T >= 1 keys per sequence */
+  int64_t head_dim;   /* D, 64 or 128 */
+} hga_shape;
+
+/* Version of this interface (HGA_ABI_VERSION of the built library). */
+int hga_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* hga_status_str(int status);
+
+/* Number of chunks ceil(T/chunk) and groups ceil(T/group) for a context of
+ * seq_len keys. chunk >= 1, group >= 1, chunk % group == 0. Either output may be
+ * NULL. */
+int hga_summary_counts(int64_t seq_len, int32_t chunk, int32_t group,
+                       int64_t* n_chunks, int64_t* n_groups);
+
+/*
+ * Step 1, summaries (HGA abstract: compact RoPE-aware chunk summaries; groups are
+ * the sub-blocks of a chunk that step 2 routes).
+ *   K          [B, Hkv, T, D], dtype `dtype`: post-RoPE keys.
+ *   chunk_mean [B, Hkv, ceil(T/chunk), D] f32, written: mean key of each chunk.
+ *   group_mean [B, Hkv, ceil(T/group), D] f32, written: mean key of each group.
+ * A short last group or chunk is the mean of the keys it has. Accumulation is
+ * fp32. chunk % group == 0; chunk / group <= 4096; group <= 65536.
+ */
+int hga_build_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
+                        int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
+                        float* chunk_mean, float* group_mean, void* stream);
+
+/*
+ * Step 1 for a grown or edited cache: recomputes, from K, the summaries of every
+ * chunk that holds a token in [t_begin, t_end) and of all groups of those chunks;
+ * the rest of chunk_mean/group_mean is left untouched. With 0 <= t_begin < t_end
+ * <= T. The recomputed values are bit-identical to what hga_build_summaries
+ * writes for them. A decode step that appended key T-1 calls it with
+ * [T-1, T). Arguments otherwise as hga_build_summaries.
+ */
+int hga_update_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
+                         int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
+                         int64_t t_begin, int64_t t_end,
+                         float* chunk_mean, float* group_mean, void* stream);
+
+/* Workspace bytes hga_route needs for this shape and these parameters. */
+int hga_route_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
+                             int32_t k_chunk, int32_t k_group, size_t* bytes);
+
+/*
+ * Step 2, two-level routing (HGA abstract: retrieve chunks by summary, then keep
+ * only the most relevant groups inside them), for every query head separately.
+ *   Q          [B, Hq, Nq, D], dtype `dtype`: post-RoPE queries.
+ *   chunk_mean, group_mean: as written by hga_build_summaries for this T.
+ *   k_chunk >= 0 chunks kept by score besides the first and the query's own;
+ *   k_group >= 1 groups kept. Limits: ceil(T/chunk) <= 4096 and
+ *   (k_chunk + 2) * (chunk/group) <= 4096 (else HGA_ERR_UNSUPPORTED).
+ *   scale      score scale; <= 0 means 1/sqrt(D).
+ *   chunk_idx  [B, Hq, Nq, k_chunk + 2] int32 or NULL, written: kept chunk ids,
+ *              ascending, -1 padded.
+ *   group_idx  [B, Hq, Nq, k_group] int32, written: kept group ids, ascending,
+ *              -1 padded.
+ * Scores are fp32; equal fp32 scores go to the lower index.
+ */
+int hga_route(const hga_shape* shape, const void* Q, int32_t dtype,
+              const float* chunk_mean, const float* group_mean, int32_t chunk, int32_t group,
+              int32_t k_chunk, int32_t k_group, float scale,
+              int32_t* chunk_idx, int32_t* group_idx,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes hga_attend needs for this shape and these parameters. */
+int hga_attend_workspace_size(const hga_shape* shape, int32_t group, int32_t k_group,
+                              size_t* bytes);
+
+/*
+ * Step 3, exact attention over the routed tokens (HGA abstract: exact
+ * token-level attention over the retrieved set only).
+ *   Q         [B, Hq, Nq, D]; K, V [B, Hkv, T, D]; all of dtype `dtype`.
+ *             K and V may live in pinned host memory the device can address
+ *             (hipHostMalloc); the kernel then reads only the routed groups.
+ *   group_idx [B, Hq, Nq, k_group] int32 group ids in [0, ceil(T/group)), as
+ *             hga_route writes them; -1 (and any id outside that range) is
+ *             ignored. Each id must appear at most once per row.
+ *   O         [B, Hq, Nq, D] of dtype `dtype`, written:
+ *             O = sum_j softmax_j(scale * q.k_j) v_j over j in the listed groups,
+ *             j <= p, with fp32 accumulation.
+ *   lse       [B, Hq, Nq] f32 or NULL, written: natural-log log-sum-exp of the
+ *             scaled logits over the same tokens.
+ *   scale     <= 0 means 1/sqrt(D).
+ * A row with no token gets O = 0 and lse = -inf.
+ */
+int hga_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
+               int32_t dtype, const int32_t* group_idx, int32_t k_group, int32_t group,
+               float scale, void* O, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

@@ -76,6 +76,13 @@ def top_k(ids, scores, k: int):
     return kept, gap
 
 
+def score(q, summary_rows, scale: float | None = None):
+    """Score of each summary row for query q: q . row * scale (scale 1/sqrt(D) by default)."""
+    q = np.asarray(q, dtype=np.float64)
+    scale = 1.0 / math.sqrt(q.shape[0]) if scale is None else scale
+    return (np.asarray(summary_rows, dtype=np.float64) @ q) * scale
+
+
 @dataclass
 class QueryRoute:
     chunks: list          # kept chunk ids, ascending
@@ -92,12 +99,9 @@ class QueryRoute:
 # --------------------------------------------------------------------------
 def route_query(q, chunk_mean_h, group_mean_h, p: int, chunk: int, group: int,
                 k_chunk: int, k_group: int, scale: float | None = None) -> QueryRoute:
-    q = np.asarray(q, dtype=np.float64)
-    D = q.shape[0]
-    scale = 1.0 / math.sqrt(D) if scale is None else scale
     n_g = group_mean_h.shape[0]
     L = p // chunk                                     # the query's own chunk
-    chunk_scores = (np.asarray(chunk_mean_h[:L + 1], dtype=np.float64) @ q) * scale
+    chunk_scores = score(q, chunk_mean_h[:L + 1], scale)
     if L + 1 <= k_chunk + 2:
         chunks, chunk_gap = list(range(L + 1)), math.inf
     else:
@@ -107,7 +111,7 @@ def route_query(q, chunk_mean_h, group_mean_h, p: int, chunk: int, group: int,
     per_chunk = chunk // group
     candidates = [g for c in chunks for g in range(c * per_chunk, (c + 1) * per_chunk)
                   if g < n_g and g * group <= p]
-    cand_scores = (np.asarray(group_mean_h[candidates], dtype=np.float64) @ q) * scale
+    cand_scores = score(q, np.asarray(group_mean_h)[candidates], scale)
     groups, group_gap = top_k(candidates, cand_scores, k_group)
     return QueryRoute(chunks, groups, chunk_scores, candidates, cand_scores,
                       chunk_gap, group_gap)

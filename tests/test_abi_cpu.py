@@ -1,0 +1,127 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every symbol
+include/hga.h declares, and rejects bad arguments on the host before anything
+is enqueued. No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_sparse_attention_summaries_amd as hga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hga.h")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hga_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    L = ctypes.CDLL(hga.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in hga.h but not exported"
+
+
+def test_version_and_status_text():
+    L = hga.lib()
+    assert L.hga_abi_version() == 1
+    for s in (OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED, 123):
+        assert len(L.hga_status_str(s)) > 0
+
+
+def test_summary_counts():
+    assert hga.summary_counts(65536, 256, 32) == (256, 2048)
+    assert hga.summary_counts(1000, 64, 16) == (16, 63)
+    L = hga.lib()
+    assert L.hga_summary_counts(100, 48, 32, None, None) == PARAM     # chunk % group != 0
+    assert L.hga_summary_counts(0, 64, 16, None, None) == SHAPE
+    assert L.hga_summary_counts(100, 0, 16, None, None) == PARAM
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # never dereferenced: every call below is rejected first
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _shape(**kw):
+    d = dict(batch=1, q_heads=32, kv_heads=4, n_queries=1, seq_len=65536, head_dim=128)
+    d.update(kw)
+    return hga.Shape(**d)
+
+
+def test_build_summaries_rejects_before_launch():
+    L = hga.lib()
+    f = L.hga_build_summaries
+    assert f(None, 1, 1, 4, 65536, 128, 256, 32, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 7, 1, 4, 65536, 128, 256, 32, FAKE, FAKE, None) == DTYPE
+    assert f(FAKE, 1, 1, 4, 65536, 96, 256, 32, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 0, 4, 65536, 128, 256, 32, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 1, 4, 65536, 128, 250, 32, FAKE, FAKE, None) == PARAM
+    assert f(MIS, 1, 1, 4, 65536, 128, 256, 32, FAKE, FAKE, None) == LAYOUT
+    u = L.hga_update_summaries
+    assert u(FAKE, 1, 1, 4, 1024, 128, 256, 32, 5, 5, FAKE, FAKE, None) == PARAM
+    assert u(FAKE, 1, 1, 4, 1024, 128, 256, 32, 0, 1025, FAKE, FAKE, None) == PARAM
+    assert u(FAKE, 1, 1, 4, 1024, 128, 256, 32, -1, 3, FAKE, FAKE, None) == PARAM
+
+
+def test_route_rejects_before_launch():
+    L = hga.lib()
+    n = ctypes.c_size_t()
+    s = _shape()
+    assert L.hga_route_workspace_size(ctypes.byref(s), 256, 32, 32, 64, ctypes.byref(n)) == OK
+    assert n.value >= 32 * (256 + 2048) * 4
+    r = L.hga_route
+    args = [FAKE, 1, FAKE, FAKE, 256, 32, 32, 64, 0.0, FAKE, FAKE, FAKE, n.value, None]
+    bad = list(args); bad[0] = None
+    assert r(ctypes.byref(s), *bad) == NULL
+    bad = list(args); bad[1] = 5
+    assert r(ctypes.byref(s), *bad) == DTYPE
+    bad = list(args); bad[12] = n.value - 1
+    assert r(ctypes.byref(s), *bad) == WORKSPACE
+    bad = list(args); bad[7] = 0
+    assert r(ctypes.byref(s), *bad) == PARAM                  # k_group < 1
+    bad = list(args); bad[6] = -1
+    assert r(ctypes.byref(s), *bad) == PARAM                  # k_chunk < 0
+    bad = list(args); bad[0] = MIS
+    assert r(ctypes.byref(s), *bad) == LAYOUT
+    assert r(ctypes.byref(_shape(kv_heads=5)), *args) == SHAPE
+    assert r(ctypes.byref(_shape(n_queries=70000)), *args) == SHAPE
+    assert r(None, *args) == NULL
+    # more chunks than one wave selects from
+    big = _shape(seq_len=1 << 21)
+    assert L.hga_route_workspace_size(ctypes.byref(big), 256, 32, 32, 64, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_attend_rejects_before_launch():
+    L = hga.lib()
+    n = ctypes.c_size_t()
+    s = _shape()
+    assert L.hga_attend_workspace_size(ctypes.byref(s), 32, 64, ctypes.byref(n)) == OK
+    a = L.hga_attend
+    args = [FAKE, FAKE, FAKE, 1, FAKE, 64, 32, 0.0, FAKE, None, FAKE, n.value, None]
+    bad = list(args); bad[1] = None
+    assert a(ctypes.byref(s), *bad) == NULL
+    bad = list(args); bad[3] = 2
+    assert a(ctypes.byref(s), *bad) == DTYPE
+    bad = list(args); bad[5] = 0
+    assert a(ctypes.byref(s), *bad) == PARAM
+    bad = list(args); bad[6] = 0
+    assert a(ctypes.byref(s), *bad) == PARAM
+    bad = list(args); bad[11] = 0
+    assert a(ctypes.byref(s), *bad) == WORKSPACE
+    bad = list(args); bad[8] = MIS
+    assert a(ctypes.byref(s), *bad) == LAYOUT
+    assert a(ctypes.byref(_shape(head_dim=80)), *args) == SHAPE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    K = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        hga.build_summaries(K, 16, 4)

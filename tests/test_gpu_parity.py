@@ -1,0 +1,150 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Workloads: the tiny fp32 case and its all-selected twin (which must equal dense
+causal attention), the 64K-context Qwen3-30B-A3B-shaped decode layer, the
+batch-16 context sweep, and edge shapes (ragged T, short and single chunks,
+k_chunk 0, padding, every position a query, MHA, r = 16, D = 64, G > 32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_summaries_amd as hga
+import oracle
+from synth import DECODE_64K, SWEEP, TINY, TINY_ALL, Workload, generate
+from tests import parity
+from tests.gpu_runner import check_workload, log, np_of, run_hip, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def test_tiny_f32():
+    log("case tiny-f32")
+    inp = generate(TINY)
+    out = run_hip(TINY, inp)
+    check_workload(TINY, inp, out)
+
+
+def test_tiny_all_selected_equals_dense():
+    log("case tiny-f32 all-selected")
+    inp = generate(TINY_ALL)
+    out = run_hip(TINY_ALL, inp)
+    check_workload(TINY_ALL, inp, out)
+    Od, lsed = oracle.dense_causal(inp.Q, inp.K, inp.V)
+    parity.check_outputs(np_of(out["O"]), np_of(out["lse"]), Od, lsed, "f32")
+    gidx = out["gidx"].cpu().numpy()
+    for i in range(TINY.Nq):   # every group up to the query's own is routed
+        p = TINY.T - TINY.Nq + i
+        assert [g for g in gidx[0, 0, i] if g >= 0] == list(range(p // TINY.group + 1))
+
+
+EDGE = [
+    # ragged T (partial last chunk and group), planted, B=2
+    Workload("edge-ragged", 2, 8, 2, 128, 5000, 1, 256, 32, 4, 12, 1e6, "bf16", 2),
+    # D=64 bf16, MHA, 3 queries with straddling groups
+    Workload("edge-d64-mha", 1, 4, 4, 64, 3000, 3, 128, 16, 3, 10, 1e4, "bf16", 0),
+    # fp32, r=16 (two 16-row blocks per KV head at Nq=2)
+    Workload("edge-f32-r16", 1, 16, 1, 128, 2048, 2, 64, 8, 5, 20, 1e4, "f32", 0),
+    # fewer keys than one chunk: only chunk 0 exists
+    Workload("edge-single-chunk", 1, 2, 1, 128, 200, 1, 256, 32, 4, 3, 1e4, "bf16", 0),
+    # no chunk picked by score: only the forced ones
+    Workload("edge-kc0", 1, 8, 2, 128, 4096, 1, 256, 32, 0, 6, 1e6, "bf16", 0),
+    # fewer candidates than k_group: -1 padding
+    Workload("edge-pad", 1, 4, 1, 128, 1024, 1, 256, 64, 1, 20, 1e4, "bf16", 0),
+    # every position is a query (p = 0 included)
+    Workload("edge-all-positions", 1, 2, 1, 64, 100, 100, 32, 8, 2, 3, 1e4, "f32", 0),
+    # group == chunk, and groups of 64 tokens (two gather tiles)
+    Workload("edge-gpc1-g64", 1, 8, 1, 128, 4096, 1, 64, 64, 6, 6, 1e6, "bf16", 0),
+    # groups of 48 tokens (a partial second tile)
+    Workload("edge-g48", 1, 4, 2, 128, 3000, 2, 96, 48, 5, 7, 1e4, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_edge_shapes(w):
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+
+
+def test_qwen3_decode_64k():
+    w = DECODE_64K
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    st, _ = check_workload(w, inp, out)
+    # planted chunks are retrieved and fill the group budget: 64 groups = 2048 tokens (3.125%)
+    gidx = out["gidx"].cpu().numpy()
+    per = w.chunk // w.group
+    for h in range(w.Hq):
+        planted = inp.planted[(0, h)]
+        assert sorted(set(g // per for g in gidx[0, h, 0])) == planted
+        assert (gidx[0, h, 0] >= 0).sum() == w.k_group
+
+
+@pytest.mark.parametrize("T", sorted(SWEEP))
+def test_sweep_b16(T):
+    w = SWEEP[T]
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    b_list = None if T <= 16384 else [0, 7, 15]
+    check_workload(w, inp, out, b_list=b_list)
+
+
+def test_update_summaries_bit_identical_to_build():
+    log("case update-summaries")
+    w = DECODE_64K.with_(T=5000, B=2)
+    inp = generate(w)
+    K = to_dev(inp.K, w.dtype)
+    cm, gm = hga.build_summaries(K, w.chunk, w.group)
+    # change keys in one place, refresh only there, compare with a full rebuild
+    K[:, :, 4100:4103] += 1.5
+    hga.update_summaries(K, w.chunk, w.group, 4100, 4103, cm, gm)
+    cm2, gm2 = hga.build_summaries(K, w.chunk, w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(cm, cm2) and torch.equal(gm, gm2)
+    # appending the last key of the cache
+    K[:, :, -1] -= 2.0
+    hga.update_summaries(K, w.chunk, w.group, w.T - 1, w.T, cm, gm)
+    cm2, gm2 = hga.build_summaries(K, w.chunk, w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(cm, cm2) and torch.equal(gm, gm2)
+
+
+def test_deterministic():
+    log("case determinism")
+    w = DECODE_64K.with_(T=16384, k_chunk=8, k_group=16, B=2)
+    inp = generate(w)
+    a = run_hip(w, inp)
+    b = run_hip(w, inp)
+    for k in ("cm", "gm", "cidx", "gidx", "O", "lse"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_explicit_scale():
+    log("case explicit-scale")
+    w = DECODE_64K.with_(T=4096, k_chunk=4, k_group=8)
+    inp = generate(w)
+    out = run_hip(w, inp, scale=0.05)
+    check_workload(w, inp, out, scale=0.05)
+
+
+def test_kv_in_pinned_host_memory():
+    log("case pinned-host-kv")
+    w = DECODE_64K.with_(T=8192, k_chunk=4, k_group=8, B=2)
+    inp = generate(w)
+    out = run_hip(w, inp)
+    Kh = torch.from_numpy(inp.K).to(torch.bfloat16).pin_memory()
+    Vh = torch.from_numpy(inp.V).to(torch.bfloat16).pin_memory()
+    O, lse = hga.attend(out["Q"], Kh, Vh, out["gidx"], w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(O, out["O"]) and torch.equal(lse, out["lse"])

@@ -16,8 +16,8 @@ MUTATIONS = {
                              "K[:, :, g * group:min((g + 1) * group, T)].sum(axis=2)"),
     "chunk-summary-off-by-one": ("K[:, :, c * chunk:min((c + 1) * chunk, T)].mean(axis=2)",
                                  "K[:, :, c * chunk + 1:min((c + 1) * chunk, T)].mean(axis=2)"),
-    "score-scale-1/D": ("scale = 1.0 / math.sqrt(D) if scale is None else scale\n    n_g",
-                        "scale = 1.0 / D if scale is None else scale\n    n_g"),
+    "score-scale-1/D": ("scale = 1.0 / math.sqrt(q.shape[0]) if scale is None else scale\n    return (np.asarray(summary_rows",
+                        "scale = 1.0 / q.shape[0] if scale is None else scale\n    return (np.asarray(summary_rows"),
     "topk-ascending": ("key=lambda t: (-scores[t], ids[t])", "key=lambda t: (scores[t], ids[t])"),
     "ties-to-higher-index": ("key=lambda t: (-scores[t], ids[t])", "key=lambda t: (-scores[t], -ids[t])"),
     "forced-wrong-last": ("chunks = sorted({0, L, *best})", "chunks = sorted({0, L - 1, *best})"),
