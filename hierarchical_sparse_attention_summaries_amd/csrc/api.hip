@@ -5,7 +5,7 @@
 #include <algorithm>
 #include <cstdint>
 
-#include "../../include/hga.h"
+#include "hga.h"
 #include "hga_internal.h"
 
 namespace hga {
@@ -56,7 +56,8 @@ int check_route_params(const hga_shape* s, int32_t chunk, int32_t group, int32_t
   const int64_t gpc = chunk / group;
   const int64_t n_g = (s->seq_len + group - 1) / group;
   const int64_t kept = std::min<int64_t>(int64_t(k_chunk) + 2, n_c);
-  if (n_c - 2 > hga::kMaxSelectItems || kept * gpc > hga::kMaxSelectItems)
+  if (n_c - 2 > hga::kMaxSelectItems || kept * gpc > hga::kMaxSelectItems ||
+      kept > hga::kMaxKeptChunks)
     return HGA_ERR_UNSUPPORTED;
   if (s->batch * s->q_heads * s->n_queries * (n_c + n_g) >= (int64_t(1) << 40))
     return HGA_ERR_SHAPE;

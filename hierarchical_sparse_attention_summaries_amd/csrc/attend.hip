@@ -21,6 +21,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 32;  // tokens per gather tile
+constexpr int kMaxSplits = 32;  // workgroups per row at most (the plan guarantees it)
 
 template <typename TKV, int D>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
   __shared__ float s_m[kWaves], s_l[kWaves];
   __shared__ float s_o[kWaves][D];
   __shared__ bool s_last;
+  __shared__ float s_part[kMaxSplits * (D + 2)];
 
   const int row = blockIdx.x / n_splits;
   const int split = blockIdx.x % n_splits;
@@ -70,53 +72,91 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
   const int e0 = (split * kWaves + wave) * groups_per_wave;
   const int e1 = min(e0 + groups_per_wave, a.k_g);
   const int n_g = (a.T + a.G - 1) / a.G;
-  for (int e = e0; e < e1; ++e) {
-    const int g = gl[e];
-    if (g < 0 || g >= n_g) continue;  // -1 padding (and ids out of range) carry no tokens
-    const int t0 = g * a.G;
-    const int t1 = min(t0 + a.G, t_lim);
-    for (int base = t0; base < t1; base += kTile) {
-      uint4 kr[NLD], vr[NLD];
+
+  // Token range [t0, t1) of list entry e (empty for -1 padding, ids out of
+  // range, and groups that start after the query).
+  auto span = [&](int e, int& t0, int& t1) {
+    const int g = e < e1 ? gl[e] : -1;
+    if (g < 0 || g >= n_g) {
+      t0 = t1 = 0;
+      return;
+    }
+    t0 = g * a.G;
+    t1 = min(t0 + a.G, t_lim);
+    if (t1 < t0) t1 = t0;
+  };
+  // Issue the loads of up to kTile tokens from `base` (rows >= t1 read as 0).
+  auto load = [&](int base, int t1, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int t = base + u * RPL + sub;
-        if (t < t1) {
-          kr[u] = ld16(Kb + static_cast<size_t>(t) * D + col);
-          vr[u] = ld16(Vb + static_cast<size_t>(t) * D + col);
-        } else {
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
-        }
+    for (int u = 0; u < NLD; ++u) {
+      const int t = base + u * RPL + sub;
+      if (t < t1) {
+        kr[u] = ld16(Kb + static_cast<size_t>(t) * D + col);
+        vr[u] = ld16(Vb + static_cast<size_t>(t) * D + col);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
       }
-      float s[NLD];
-      float mt = -INFINITY;
+    }
+  };
+  // Fold one loaded tile into (m, l, o). Token `base` must be valid.
+  auto consume = [&](int base, int t1, const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
+    float sc[NLD];
+    float mt = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        float x[EPL];
-        widen(kr[u], x);
-        float d = 0.f;
+    for (int u = 0; u < NLD; ++u) {
+      float x[EPL];
+      widen(kr[u], x);
+      float d = 0.f;
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) d = fmaf(q[k], x[k], d);
-        d = group_sum<LPR>(d);
-        s[u] = (base + u * RPL + sub < t1) ? d : -INFINITY;
-        mt = fmaxf(mt, s[u]);
+      for (int k = 0; k < EPL; ++k) d = fmaf(q[k], x[k], d);
+      d = group_sum<LPR>(d);
+      sc[u] = (base + u * RPL + sub < t1) ? d : -INFINITY;
+      mt = fmaxf(mt, sc[u]);
+    }
+    mt = across_rows_max<LPR>(mt);
+    const float m_new = fmaxf(m, mt);  // finite: token `base` is valid
+    const float corr = exp2f(m - m_new);
+    l *= corr;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) o[k] *= corr;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const float pu = exp2f(sc[u] - m_new);
+      l += pu;
+      float x[EPL];
+      widen(vr[u], x);
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) o[k] = fmaf(pu, x[k], o[k]);
+    }
+    m = m_new;
+  };
+
+  if (a.G <= kTile) {
+    // One tile per group. Two register buffers: the next group's keys and
+    // values are in flight while the current one is folded in.
+    uint4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
+    int a0, a1, b0, b1;
+    span(e0, a0, a1);
+    load(a0, a1, kA, vA);
+    for (int e = e0; e < e1; e += 2) {
+      span(e + 1, b0, b1);
+      load(b0, b1, kB, vB);
+      if (a0 < a1) consume(a0, a1, kA, vA);
+      span(e + 2, a0, a1);
+      load(a0, a1, kA, vA);
+      if (b0 < b1) consume(b0, b1, kB, vB);
+    }
+  } else {
+    // Groups longer than a tile: walk their tiles one by one.
+    uint4 kA[NLD], vA[NLD];
+    for (int e = e0; e < e1; ++e) {
+      int t0, t1;
+      span(e, t0, t1);
+      for (int base = t0; base < t1; base += kTile) {
+        load(base, t1, kA, vA);
+        consume(base, t1, kA, vA);
       }
-      mt = across_rows_max<LPR>(mt);
-      const float m_new = fmaxf(m, mt);  // finite: token `base` is always valid
-      const float corr = exp2f(m - m_new);
-      l *= corr;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) o[k] *= corr;
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const float pu = exp2f(s[u] - m_new);
-        l += pu;
-        float x[EPL];
-        widen(vr[u], x);
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) o[k] = fmaf(pu, x[k], o[k]);
-      }
-      m = m_new;
     }
   }
   // Lanes of one column slot hold disjoint token rows: fold them.
@@ -165,23 +205,38 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
     return;
   }
   float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
-  if (d < D) part[2 + d] = acc;
+  if (d < D) store_shared(part + 2 + d, acc);
   if (d == 0) {
-    part[0] = M;
-    part[1] = Lsum;
+    store_shared(part, M);
+    store_shared(part + 1, Lsum);
   }
   if (!arrive_last(a.counters + row, static_cast<unsigned>(n_splits), &s_last)) return;
 
+  // Pull every split's (m, l, o) into LDS with all loads in flight at once.
   const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
+  const int total = n_splits * (D + 2);
+  for (int base = 0; base < total; base += 4 * kThreads) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + u * kThreads + threadIdx.x;
+      v[u] = idx < total ? load_shared(rp + idx) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + u * kThreads + threadIdx.x;
+      if (idx < total) s_part[idx] = v[u];
+    }
+  }
+  __syncthreads();
   float Mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, rp[s * (D + 2)]);
+  for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, s_part[s * (D + 2)]);
   float Lx = 0.f, ox = 0.f;
   if (Mx != -INFINITY) {
     for (int s = 0; s < n_splits; ++s) {
-      const float ms = rp[s * (D + 2)];
-      const float f = exp2f(ms - Mx);
-      Lx += rp[s * (D + 2) + 1] * f;
-      if (d < D) ox += rp[s * (D + 2) + 2 + d] * f;
+      const float f = exp2f(s_part[s * (D + 2)] - Mx);
+      Lx += s_part[s * (D + 2) + 1] * f;
+      if (d < D) ox += s_part[s * (D + 2) + 2 + d] * f;
     }
   }
   finish(Mx, Lx, ox);
@@ -202,12 +257,15 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g) {
   AttendPlan pl{};
-  // Enough waves to keep every CU's memory pipe busy (>= 16 waves per CU), no
-  // more: larger groups_per_wave means fewer partials to merge.
-  const int64_t target_waves = 16 * static_cast<int64_t>(device_cu_count());
+  // Enough waves to keep every CU's memory pipe busy (each wave keeps two
+  // groups in flight), no more: larger groups_per_wave means fewer partials
+  // to merge and fewer workgroups bumping one arrival counter.
+  const int64_t target_waves = 4 * static_cast<int64_t>(device_cu_count());
   int gpw = 1;
   while (gpw < 16 && rows * ((k_g + 2 * gpw - 1) / (2 * gpw)) >= target_waves) gpw *= 2;
   (void)G;
+  // at most kMaxSplits workgroups (of kWaves waves) per row
+  while ((k_g + gpw - 1) / gpw > kMaxSplits * kWaves) gpw *= 2;
   pl.groups_per_wave = gpw;
   const int waves_per_row = (k_g + gpw - 1) / gpw;
   pl.n_splits = (waves_per_row + kWaves - 1) / kWaves;

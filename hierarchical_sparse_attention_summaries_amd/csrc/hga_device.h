@@ -103,19 +103,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 template <int E>
 __device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) {
   // Largest threshold t with #(key >= t) >= k, found bit by bit from the top:
-  // that is the k-th largest key.
+  // that is the k-th largest key. Stop early once exactly k keys are >= t: the
+  // chosen set is then fixed whatever the lower bits.
   uint32_t thr = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t t = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) cnt += __popcll(ballot(key[e] >= t));
-    if (cnt >= k) thr = t;
+    if (cnt >= k) {
+      thr = t;
+      if (cnt == k) break;
+    }
   }
   int above = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) above += __popcll(ballot(key[e] > thr));
   const int need = k - above;  // keys equal to thr still to take, lowest index first
+                               // (all of them after an early stop)
   uint32_t chosen = 0;
   int eq_before = 0;
 #pragma unroll
@@ -130,24 +135,36 @@ __device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) 
 }
 
 // ---------------------------------------------------------------- grid-level hand-off
-// Called by every thread of a workgroup after it stored its results. Returns
-// true in exactly one workgroup of the `total` that share `counter`: the last to
-// arrive, which then sees every other workgroup's stores. That workgroup resets
-// the counter to zero for the next call. No workgroup waits on another.
+// Data one workgroup hands to another goes through agent-scope relaxed atomics:
+// on gfx950 those are coherent across the 8 XCDs' L2s by themselves (stores
+// write through, loads read the coherent copy), so no workgroup has to write
+// back or invalidate its whole L2 as an agent-scope fence would.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of a workgroup after it issued its store_shared()
+// results. Returns true in exactly one workgroup of the `total` that share
+// `counter`: the last to arrive, which can then read every other workgroup's
+// results with load_shared(). That workgroup resets the counter to zero for the
+// next call. No workgroup ever waits for another.
 __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, bool* s_flag) {
-  __threadfence();  // release this workgroup's stores at device (agent) scope
+  // Every store of this thread is performed (acknowledged at the coherence
+  // point) before the workgroup counts itself in.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev == total - 1;
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = last;
   }
   __syncthreads();
-  const bool last = *s_flag;
-  if (last) __threadfence();  // acquire: drop stale cached copies before reading
-  return last;
+  return *s_flag;
 }
 
 }  // namespace hga

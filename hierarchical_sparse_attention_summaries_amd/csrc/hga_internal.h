@@ -12,8 +12,9 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 // Largest number of items one wave selects from (middle chunks, or candidate
-// groups of the kept chunks).
+// groups of the kept chunks), and of chunks one query keeps.
 constexpr int kMaxSelectItems = 4096;
+constexpr int kMaxKeptChunks = 1024;
 
 hipError_t launch_summaries(const void* K, int dtype, int64_t BH, int64_t D, int64_t T,
                             int C, int G, int c_begin, int c_end, float* chunk_mean,

@@ -25,8 +25,8 @@
 namespace hga {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;  // one query row per wave in the selection
 constexpr int kMaxRows = 16;
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -36,7 +36,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Selection for one query row, run by one whole wave.
 template <int E>
-__device__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
+__device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
   const int lane = lane_id();
   const int L = p / a.C;  // the query's own chunk
   const float* cs = a.chunk_scores + static_cast<size_t>(row) * a.n_c;
@@ -57,7 +57,7 @@ __device__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int t = e * kWave + lane;
-        key[e] = t < L - 1 ? order_key(cs[1 + t]) : 0u;
+        key[e] = t < L - 1 ? order_key(load_shared(cs + 1 + t)) : 0u;
       }
       const uint32_t chosen = wave_top_k<E>(key, a.k_c);
       int before = 0;
@@ -90,7 +90,7 @@ __device__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
       valid = g < a.n_g && static_cast<int64_t>(g) * a.G <= p;
     }
     gid[e] = g;
-    key[e] = valid ? order_key(gs[g]) : 0u;
+    key[e] = valid ? order_key(load_shared(gs + g)) : 0u;
     n_valid += __popcll(ballot(valid));
   }
   uint32_t chosen = 0;
@@ -121,7 +121,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
   constexpr int LPR = D / DPL;    // lanes per summary row
   constexpr int RPS = kWave / LPR;
   extern __shared__ int s_kept_all[];
-  __shared__ float s_q[RM][D];
   __shared__ bool s_last;
 
   const int unit = blockIdx.x / n_splits;
@@ -143,29 +142,35 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
     return (b * a.Hq + h) * a.Nq + i;
   };
 
-  for (int idx = threadIdx.x; idx < RM * D; idx += kThreads) {
-    const int rho = idx / D;
-    const int d = idx % D;
-    float v = 0.f;
-    if (rho < rows_here) {
-      const size_t off = static_cast<size_t>(row_of(rho)) * D + d;
-      if constexpr (sizeof(TQ) == 4) {
-        v = static_cast<const float*>(a.Q)[off];
-      } else {
-        v = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.Q)[off]) << 16);
-      }
-    }
-    s_q[rho][d] = v * a.scale;
-  }
-  __syncthreads();
-
+  // Each lane keeps, for every query row of the block, the 8 query dims it
+  // multiplies (loaded straight into registers, scaled).
   const int sub = lane / LPR;
   const int col = (lane % LPR) * DPL;
   float qr[RM][DPL];
 #pragma unroll
-  for (int rho = 0; rho < RM; ++rho)
+  for (int rho = 0; rho < RM; ++rho) {
+    if (rho < rows_here) {
+      const size_t off = static_cast<size_t>(row_of(rho)) * D + col;
+      if constexpr (sizeof(TQ) == 4) {
+        float x0[4], x1[4];
+        widen(ld16(static_cast<const float*>(a.Q) + off), x0);
+        widen(ld16(static_cast<const float*>(a.Q) + off + 4), x1);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qr[rho][e] = s_q[rho][col + e];
+        for (int e = 0; e < 4; ++e) {
+          qr[rho][e] = x0[e] * a.scale;
+          qr[rho][4 + e] = x1[e] * a.scale;
+        }
+      } else {
+        float x[8];
+        widen(ld16(static_cast<const uint16_t*>(a.Q) + off), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[rho][e] = x[e] * a.scale;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) qr[rho][e] = 0.f;
+    }
+  }
 
   const int c_lo = split * chunks_per_split;
   const int c_hi = min(c_lo + chunks_per_split, a.n_c);
@@ -174,44 +179,44 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
   const float* cm = a.chunk_mean + static_cast<size_t>(b * a.Hkv + kv) * a.n_c * D;
   const float* gm = a.group_mean + static_cast<size_t>(b * a.Hkv + kv) * a.n_g * D;
 
-  for (int base = wave * RPS; base < n_items; base += kWaves * RPS) {
-    const int item = base + sub;
-    bool valid = item < n_items;
-    const float* src = nullptr;
-    float* dst_base = nullptr;
-    int dst_col = 0, dst_stride = 0;
-    if (valid) {
-      if (item < n_ch) {
-        dst_col = c_lo + item;
-        src = cm + static_cast<size_t>(dst_col) * D;
-        dst_base = a.chunk_scores;
-        dst_stride = a.n_c;
+  // Summary rows of this workgroup, kBatch wave-steps of loads in flight at a time.
+  constexpr int kBatch = 4;
+  constexpr int kStride = kWaves * RPS;
+  for (int base0 = wave * RPS; base0 < n_items; base0 += kBatch * kStride) {
+    float sv[kBatch][DPL];
+    int dst_col[kBatch];
+    bool valid[kBatch], is_chunk[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int item = base0 + j * kStride + sub;
+      is_chunk[j] = item < n_ch;
+      dst_col[j] = is_chunk[j] ? c_lo + item : c_lo * a.gpc + (item - n_ch);
+      valid[j] = item < n_items && (is_chunk[j] || dst_col[j] < a.n_g);
+      if (valid[j]) {
+        const float* src = (is_chunk[j] ? cm : gm) + static_cast<size_t>(dst_col[j]) * D + col;
+        const float4 v0 = *reinterpret_cast<const float4*>(src);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+        sv[j][0] = v0.x; sv[j][1] = v0.y; sv[j][2] = v0.z; sv[j][3] = v0.w;
+        sv[j][4] = v1.x; sv[j][5] = v1.y; sv[j][6] = v1.z; sv[j][7] = v1.w;
       } else {
-        dst_col = c_lo * a.gpc + (item - n_ch);
-        valid = dst_col < a.n_g;
-        src = gm + static_cast<size_t>(dst_col) * D;
-        dst_base = a.group_scores;
-        dst_stride = a.n_g;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) sv[j][e] = 0.f;
       }
     }
-    float s[DPL];
-    if (valid) {
-      float4 v0 = *reinterpret_cast<const float4*>(src + col);
-      float4 v1 = *reinterpret_cast<const float4*>(src + col + 4);
-      s[0] = v0.x; s[1] = v0.y; s[2] = v0.z; s[3] = v0.w;
-      s[4] = v1.x; s[5] = v1.y; s[6] = v1.z; s[7] = v1.w;
-    } else {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) s[e] = 0.f;
-    }
+    for (int j = 0; j < kBatch; ++j) {
+      if (base0 + j * kStride >= n_items) break;  // wave-uniform
+      float* dst_base = is_chunk[j] ? a.chunk_scores : a.group_scores;
+      const int dst_stride = is_chunk[j] ? a.n_c : a.n_g;
 #pragma unroll
-    for (int rho = 0; rho < RM; ++rho) {
-      float d = 0.f;
+      for (int rho = 0; rho < RM; ++rho) {
+        float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) d = fmaf(qr[rho][e], s[e], d);
-      d = group_sum<LPR>(d);
-      if (valid && rho < rows_here && (lane % LPR) == (rho % LPR))
-        dst_base[static_cast<size_t>(row_of(rho)) * dst_stride + dst_col] = d;
+        for (int e = 0; e < DPL; ++e) d = fmaf(qr[rho][e], sv[j][e], d);
+        d = group_sum<LPR>(d);
+        if (valid[j] && rho < rows_here && (lane % LPR) == (rho % LPR))
+          store_shared(dst_base + static_cast<size_t>(row_of(rho)) * dst_stride + dst_col[j], d);
+      }
     }
   }
 
@@ -224,7 +229,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
     switch (e_sel) {
       case 1: select_row<1>(a, row, p, s_kept); break;
       case 2: select_row<2>(a, row, p, s_kept); break;
+      case 3: select_row<3>(a, row, p, s_kept); break;
       case 4: select_row<4>(a, row, p, s_kept); break;
+      case 5: select_row<5>(a, row, p, s_kept); break;
+      case 6: select_row<6>(a, row, p, s_kept); break;
       case 8: select_row<8>(a, row, p, s_kept); break;
       case 16: select_row<16>(a, row, p, s_kept); break;
       case 32: select_row<32>(a, row, p, s_kept); break;
@@ -262,9 +270,13 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   const int64_t n_g = (T + G - 1) / G;
   pl.q_per_block = kMaxRows;
   pl.n_qblocks = static_cast<int>((r * Nq + kMaxRows - 1) / kMaxRows);
+  // Few workgroups per arrival counter (they bump it one after another), but
+  // at most 16 chunks (16 * (1 + chunk/group) summary rows) per workgroup.
   const int64_t units = B * Hkv * pl.n_qblocks;
-  const int64_t target = 2 * static_cast<int64_t>(device_cu_count());
+  const int64_t target = static_cast<int64_t>(device_cu_count()) / 2;
   int64_t splits = (target + units - 1) / units;
+  const int64_t min_splits = (n_c + 15) / 16;
+  if (splits < min_splits) splits = min_splits;
   if (splits < 1) splits = 1;
   if (splits > n_c) splits = n_c;
   pl.chunks_per_split = static_cast<int>((n_c + splits - 1) / splits);
@@ -283,8 +295,15 @@ hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hi
   const int rm = max_rows <= 8 ? 8 : 16;
   const int kept = a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2;
   const int items = (a.n_c - 2 > kept * a.gpc) ? a.n_c - 2 : kept * a.gpc;
-  int e_sel = 1;
-  while (e_sel * kWave < items) e_sel *= 2;
+  // registers per lane for the selection keys: the smallest variant that fits
+  const int need = (items + kWave - 1) / kWave;
+  int e_sel = 64;
+  for (int e : {1, 2, 3, 4, 5, 6, 8, 16, 32, 64}) {
+    if (e >= need) {
+      e_sel = e;
+      break;
+    }
+  }
   const int kept_per_wave = a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2;
   const size_t lds = static_cast<size_t>(kWaves) * kept_per_wave * sizeof(int);
   if (dtype == kF32)

@@ -14,7 +14,7 @@
 namespace hga {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: one group of a 256-token chunk each
 constexpr int kWaves = kThreads / kWave;
 
 template <typename TK, int D>

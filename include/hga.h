@@ -123,8 +123,10 @@ int hga_route_workspace_size(const hga_shape* shape, int32_t chunk, int32_t grou
  *   Q          [B, Hq, Nq, D], dtype `dtype`: post-RoPE queries.
  *   chunk_mean, group_mean: as written by hga_build_summaries for this T.
  *   k_chunk >= 0 chunks kept by score besides the first and the query's own;
- *   k_group >= 1 groups kept. Limits: ceil(T/chunk) <= 4096 and
- *   (k_chunk + 2) * (chunk/group) <= 4096 (else HGA_ERR_UNSUPPORTED).
+ *   k_group >= 1 groups kept. Limits: ceil(T/chunk) <= 4098,
+ *   min(k_chunk + 2, ceil(T/chunk)) <= 1024 and
+ *   min(k_chunk + 2, ceil(T/chunk)) * (chunk/group) <= 4096 (else
+ *   HGA_ERR_UNSUPPORTED).
  *   scale      score scale; <= 0 means 1/sqrt(D).
  *   chunk_idx  [B, Hq, Nq, k_chunk + 2] int32 or NULL, written: kept chunk ids,
  *              ascending, -1 padded.

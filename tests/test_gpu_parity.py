@@ -148,3 +148,27 @@ def test_kv_in_pinned_host_memory():
     O, lse = hga.attend(out["Q"], Kh, Vh, out["gidx"], w.group)
     torch.cuda.synchronize()
     assert torch.equal(O, out["O"]) and torch.equal(lse, out["lse"])
+
+
+def test_back_to_back_calls_share_workspace():
+    """Two different inputs of one shape through the same workspaces, with no
+    synchronisation between them: the second call must not see the first
+    call's cross-workgroup partials or scores."""
+    log("case back-to-back")
+    w = DECODE_64K.with_(T=16384, k_chunk=8, k_group=16)
+    a = generate(w, seed=11)
+    b = generate(w, seed=12)
+    Qa, Ka, Va = (to_dev(x, w.dtype) for x in (a.Q, a.K, a.V))
+    Qb, Kb, Vb = (to_dev(x, w.dtype) for x in (b.Q, b.K, b.V))
+    cma, gma = hga.build_summaries(Ka, w.chunk, w.group)
+    cmb, gmb = hga.build_summaries(Kb, w.chunk, w.group)
+    outs = []
+    for Q, K, V, cm, gm in ((Qa, Ka, Va, cma, gma), (Qb, Kb, Vb, cmb, gmb), (Qa, Ka, Va, cma, gma)):
+        cidx, gidx = hga.route(Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
+        O, lse = hga.attend(Q, K, V, gidx, w.group)
+        outs.append(dict(Q=Q, cm=cm, gm=gm, cidx=cidx, gidx=gidx, O=O, lse=lse))
+    torch.cuda.synchronize()
+    check_workload(w, a, outs[0])
+    check_workload(w, b, outs[1])
+    check_workload(w, a, outs[2])
+    assert torch.equal(outs[0]["O"], outs[2]["O"])
