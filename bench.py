@@ -282,24 +282,26 @@ def measure(w, args, primary: bool):
     def pct(a, q):
         return a[min(len(a) - 1, int(round(q * (len(a) - 1))))]
 
-    # ---------------- per-kernel durations: HIP events around each launch on
-    # the stream the kernels run on (torch's current stream), eager launches.
+    # ---------------- per-kernel durations: HIP events on the stream the
+    # kernels run on (torch's current stream) around n back-to-back eager
+    # launches of one kernel (rotating over the copies), the GPU kept busy
+    # while the host enqueues; average = elapsed / n.
     n_k = max(50, min(args.steps, 400))
     names = ("update", "route", "attend")
     fns = (k_update, k_route, k_attend)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3 * n_k)]
-    busy_gpu()
-    for k in range(n_k):
-        for j, fn in enumerate(fns):
-            e0, e1 = ev[3 * k + j]
-            e0.record()
-            fn(k % S)
-            e1.record()
-    torch.cuda.synchronize()
     kern_us = {}
-    for j, nm in enumerate(names):
-        d = [ev[3 * k + j][0].elapsed_time(ev[3 * k + j][1]) * 1e3 for k in range(n_k)]
-        kern_us[nm] = {"avg": statistics.fmean(d), "p50": statistics.median(d)}
+    for nm, fn in zip(names, fns):
+        reps = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            busy_gpu()
+            e0.record()
+            for k in range(n_k):
+                fn(k % S)
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) * 1e3 / n_k)
+        kern_us[nm] = {"avg": statistics.median(reps), "launches": 3 * n_k}
     attend_us = kern_us["attend"]["avg"]
     achieved = attend_bytes / (attend_us * 1e-6) / 1e9
 
@@ -337,7 +339,7 @@ def measure(w, args, primary: bool):
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,
-        "kernels_us": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern_us.items()},
+        "kernels_us": {k: round(v["avg"], 3) for k, v in kern_us.items()},
         "latency_us": {"p50": round(pct(lat, 0.5), 2), "p95": round(pct(lat, 0.95), 2),
                        "p99": round(pct(lat, 0.99), 2)},
         "cpu_baseline": cpu,
