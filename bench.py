@@ -33,6 +33,7 @@ METRIC = "routed-attn decode tokens/s + achieved HBM GB/s at 64K ctx, 1 MI355X"
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 SECONDARY = "qwen3-30b-a3b-decode-b16-t65536"   # the 64K point of the batch-16 context sweep
+HOST_TIER = "qwen3-30b-a3b-host-tier-b4-t262144"  # full K/V in pinned host memory
 
 
 def parse():
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--only", choices=["attend", "route", "update", "step", "copy"])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the batch-16 64K-context point of the context sweep")
+    ap.add_argument("--no-host-tier", action="store_true",
+                    help="skip the 256K-context batch-4 run with K/V in pinned host memory")
     return ap.parse_args()
 
 
@@ -108,6 +111,12 @@ def main():
         return
 
     out = measure(w, args, primary=True)
+    if not args.no_host_tier and w.name != HOST_TIER:
+        h_args = argparse.Namespace(**vars(args))
+        h_args.steps, h_args.warmup = 10, 2
+        ht = measure(ALL[HOST_TIER], h_args, primary=False)
+        out["host_tier"] = {k: ht[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
+                                               "kernels_us", "host_tier")}
     if not args.no_secondary:
         w2 = ALL[SECONDARY]
         if w2.name != w.name:
@@ -135,8 +144,12 @@ def measure(w, args, primary: bool):
     t_gen = time.time() - t_gen
 
     Q = torch.from_numpy(inp.Q).to(dev, tdt)
-    K0 = torch.from_numpy(inp.K).to(dev, tdt)
-    V0 = torch.from_numpy(inp.V).to(dev, tdt)
+    if w.host_kv:   # full K/V in pinned host memory; summaries, Q, O in HBM
+        K0 = torch.from_numpy(inp.K).to(tdt).pin_memory()
+        V0 = torch.from_numpy(inp.V).to(tdt).pin_memory()
+    else:
+        K0 = torch.from_numpy(inp.K).to(dev, tdt)
+        V0 = torch.from_numpy(inp.V).to(dev, tdt)
     cm0, gm0 = hga.build_summaries(K0, w.chunk, w.group)
     _, gidx0 = hga.route(Q, cm0, gm0, w.T, w.chunk, w.group, w.k_chunk, w.k_group, want_chunks=False)
     torch.cuda.synchronize()
@@ -155,14 +168,18 @@ def measure(w, args, primary: bool):
     n_c, n_g = w.n_chunks, w.n_groups
     attend_bytes = routed_tokens * w.D * 2 * esize + rows * (2 * w.D * esize + 4 * w.k_group + 4)
     route_bytes = w.B * w.Hkv * (n_c + n_g) * w.D * 4 + rows * w.D * esize + rows * 4 * w.k_group
-    last_chunk_tokens = w.T - (w.T - 1) // w.chunk * w.chunk
-    update_bytes = w.B * w.Hkv * (last_chunk_tokens * w.D * esize + (1 + w.chunk // w.group) * w.D * 4)
+    c_first = (w.T - w.Nq) // w.chunk              # chunks holding the newest Nq keys
+    n_upd = w.n_chunks - c_first
+    upd_tokens = w.T - c_first * w.chunk
+    update_bytes = w.B * w.Hkv * (upd_tokens * w.D * esize + n_upd * (1 + w.chunk // w.group) * w.D * 4)
     step_bytes = attend_bytes + route_bytes + update_bytes
 
     # Cold-cache rotation: copies at distinct addresses so that one rotation's
     # routed working sets exceed the Infinity Cache.
     per_set = attend_bytes + route_bytes
     S = args.sets or max(2, min(64, -(-2 * MALL_BYTES // per_set)))
+    if w.host_kv:
+        S = 1   # host memory is not kept in the GPU caches between steps
     sets = []
     for s in range(S):
         K = K0 if s == 0 else K0.clone()
@@ -181,7 +198,7 @@ def measure(w, args, primary: bool):
 
     def k_update(s):
         K, V, cm, gm = sets[s]
-        hga.update_summaries(K, w.chunk, w.group, w.T - 1, w.T, cm, gm)
+        hga.update_summaries(K, w.chunk, w.group, w.T - w.Nq, w.T, cm, gm)
 
     def k_route(s):
         K, V, cm, gm = sets[s]
@@ -305,6 +322,17 @@ def measure(w, args, primary: bool):
     attend_us = kern_us["attend"]["avg"]
     achieved = attend_bytes / (attend_us * 1e-6) / 1e9
 
+    quality = None
+    if primary and not w.host_kv and w.Nq == 1:
+        quality = quality_proxy(hga, torch, w, Q, sets[0][0], sets[0][1], gidx0)
+    host = None
+    if w.host_kv:
+        kv_bytes = 2 * K0.numel() * esize
+        hbm = sum(t.numel() * t.element_size() for t in (Q, cm0, gm0, O, lse, gidx0, ws_r, ws_a))
+        host = {"kv_bytes_in_host_memory": kv_bytes, "hbm_bytes_resident": hbm,
+                "fetched_bytes_per_token": attend_bytes // (w.B * w.Nq),
+                "host_link_gbs": round(attend_bytes / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
+
     traffic, tinfo = stored_traffic(w.name)
     roofline = {"kernel": "hga_attend", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -335,7 +363,7 @@ def measure(w, args, primary: bool):
                    "k_chunk": w.k_chunk, "k_group": w.k_group,
                    "routed_fraction": round(routed_tokens / (rows * w.T), 5),
                    "cold_cache_copies": S, "hip_graph": use_graph,
-                   "step": "update_summaries(last key) + route + attend"},
+                   "step": "update_summaries(newest Nq keys) + route + attend"},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,
@@ -345,8 +373,34 @@ def measure(w, args, primary: bool):
         "cpu_baseline": cpu,
         "setup_s": {"generate": round(t_gen, 1)},
     }
+    if quality is not None:
+        out["quality_vs_dense"] = quality
+    if host is not None:
+        out["host_tier"] = host
     del sets, graphs_keep
     return out
+
+
+def quality_proxy(hga, torch, w, Q, K, V, gidx):
+    """Synthetic stand-in for a quality comparison with dense attention: the
+    same kernel run over every group (dense causal attention) next to the routed
+    run. Per query head: the share of the dense softmax mass that lies on the
+    routed tokens (exp(lse_routed - lse_dense)), the relative L2 error of O, and
+    the lse gap in nats."""
+    all_g = torch.arange(w.n_groups, dtype=torch.int32, device=Q.device)
+    all_g = all_g.expand(w.B, w.Hq, w.Nq, w.n_groups).contiguous()
+    Od, lsed = hga.attend(Q, K, V, all_g, w.group)
+    Or, lser = hga.attend(Q, K, V, gidx, w.group)
+    torch.cuda.synchronize()
+    mass = torch.exp(lser - lsed).flatten()
+    err = ((Or.float() - Od.float()).norm(dim=-1) / Od.float().norm(dim=-1)).flatten()
+    gap = (lsed - lser).flatten()
+    return {"mass_on_routed_mean": round(float(mass.mean()), 5),
+            "mass_on_routed_min": round(float(mass.min()), 5),
+            "rel_err_O_mean": round(float(err.mean()), 5),
+            "rel_err_O_max": round(float(err.max()), 5),
+            "lse_gap_nats_mean": round(float(gap.mean()), 5),
+            "routed_fraction": round(w.k_group * w.group / w.T, 5)}
 
 
 def cpu_baseline(w, inp, seconds):

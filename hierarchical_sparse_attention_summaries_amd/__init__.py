@@ -133,22 +133,28 @@ def summary_counts(seq_len: int, chunk: int, group: int):
     return nc.value, ng.value
 
 
+def _gpu_of(t: torch.Tensor) -> torch.device:
+    return t.device if t.is_cuda else torch.device("cuda", torch.cuda.current_device())
+
+
 def build_summaries(K: torch.Tensor, chunk: int, group: int, chunk_mean=None, group_mean=None):
-    """Mean key per chunk and per group. K [B, Hkv, T, D] -> ([B,Hkv,n_c,D], [B,Hkv,n_g,D]) f32."""
-    _need(K, "K", 4)
+    """Mean key per chunk and per group. K [B, Hkv, T, D] -> ([B,Hkv,n_c,D], [B,Hkv,n_g,D]) f32.
+    K may be a pinned host tensor (read in place); the summaries live on the GPU."""
+    _need(K, "K", 4, host_ok=True)
     B, H, T, D = K.shape
     n_c, n_g = summary_counts(T, chunk, group)
+    dev = _gpu_of(K)
     if chunk_mean is None:
-        chunk_mean = torch.empty((B, H, n_c, D), dtype=torch.float32, device=K.device)
+        chunk_mean = torch.empty((B, H, n_c, D), dtype=torch.float32, device=dev)
     if group_mean is None:
-        group_mean = torch.empty((B, H, n_g, D), dtype=torch.float32, device=K.device)
+        group_mean = torch.empty((B, H, n_g, D), dtype=torch.float32, device=dev)
     _need(chunk_mean, "chunk_mean", 4)
     _need(group_mean, "group_mean", 4)
     if tuple(chunk_mean.shape) != (B, H, n_c, D) or tuple(group_mean.shape) != (B, H, n_g, D) \
             or chunk_mean.dtype != torch.float32 or group_mean.dtype != torch.float32:
         raise ValueError("summary buffers must be float32 [B, Hkv, n, D]")
     _check(_lib.hga_build_summaries(_ptr(K), _dtype_code(K), B, H, T, D, chunk, group,
-                                    _ptr(chunk_mean), _ptr(group_mean), _stream(K.device)),
+                                    _ptr(chunk_mean), _ptr(group_mean), _stream(dev)),
            "hga_build_summaries")
     return chunk_mean, group_mean
 
@@ -156,7 +162,7 @@ def build_summaries(K: torch.Tensor, chunk: int, group: int, chunk_mean=None, gr
 def update_summaries(K: torch.Tensor, chunk: int, group: int, t_begin: int, t_end: int,
                      chunk_mean: torch.Tensor, group_mean: torch.Tensor):
     """Recompute the summaries of the chunks (and their groups) touching [t_begin, t_end)."""
-    _need(K, "K", 4)
+    _need(K, "K", 4, host_ok=True)
     _need(chunk_mean, "chunk_mean", 4)
     _need(group_mean, "group_mean", 4)
     B, H, T, D = K.shape
@@ -164,7 +170,8 @@ def update_summaries(K: torch.Tensor, chunk: int, group: int, t_begin: int, t_en
     if tuple(chunk_mean.shape) != (B, H, n_c, D) or tuple(group_mean.shape) != (B, H, n_g, D):
         raise ValueError("summary buffers do not match K")
     _check(_lib.hga_update_summaries(_ptr(K), _dtype_code(K), B, H, T, D, chunk, group, t_begin,
-                                     t_end, _ptr(chunk_mean), _ptr(group_mean), _stream(K.device)),
+                                     t_end, _ptr(chunk_mean), _ptr(group_mean),
+                                     _stream(chunk_mean.device)),
            "hga_update_summaries")
 
 

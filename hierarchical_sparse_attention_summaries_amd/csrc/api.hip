@@ -28,7 +28,7 @@ int dtype_ok(int32_t dtype) { return dtype == HGA_F32 || dtype == HGA_BF16; }
 
 int check_chunking(int64_t T, int32_t chunk, int32_t group) {
   if (chunk < 1 || group < 1 || chunk % group != 0) return HGA_ERR_PARAM;
-  if (group > 65536 || chunk / group > 4096) return HGA_ERR_PARAM;
+  if (group > 65536 || chunk / group > 512) return HGA_ERR_PARAM;
   if (T < 1 || T >= kMaxDim) return HGA_ERR_SHAPE;
   return HGA_OK;
 }
@@ -187,7 +187,12 @@ int hga_route(const hga_shape* shape, const void* Q, int32_t dtype, const float*
   a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
   a.chunk_scores = reinterpret_cast<float*>(ws + plan.off_chunk_scores);
   a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
-  const hipError_t e = hga::launch_route(a, dtype, plan, as_stream(stream));
+  a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
+  const hipError_t e =
+      (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
+                                         shape->n_queries, shape->head_dim))
+          ? hga::launch_route_prefill(a, as_stream(stream))
+          : hga::launch_route(a, dtype, plan, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 

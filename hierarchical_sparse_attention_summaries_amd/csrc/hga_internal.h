@@ -25,7 +25,9 @@ struct RoutePlan {
   int n_qblocks;        // ceil(Nq / q_per_block)
   int chunks_per_split; // chunks (and their groups) scored per workgroup
   int n_splits;         // workgroups per (sequence, KV head, query block)
-  size_t off_counters, off_chunk_scores, off_group_scores, bytes;
+  size_t off_counters, off_chunk_scores, off_group_scores;
+  size_t off_split;     // bf16 hi/lo copies of the summaries (prefill path), or 0
+  size_t bytes;
 };
 RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int C, int G,
                      int k_c, int k_g);
@@ -43,8 +45,14 @@ struct RouteArgs {
   float* chunk_scores; // workspace [B*Hq*Nq, n_c]
   float* group_scores; // workspace [B*Hq*Nq, n_g]
   unsigned* counters;  // workspace [B*Hkv*n_qblocks]
+  uint16_t* split;     // workspace [B*Hkv, 2, n_c + n_g, D] bf16 (hi, lo); prefill path only
 };
 hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hipStream_t stream);
+
+// Many query rows per KV head (chunked prefill, bf16): MFMA scoring kernel plus
+// a one-wave-per-row select kernel, over the same workspace layout.
+bool use_prefill_route(int dtype, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D);
+hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 
 struct AttendPlan {
   int groups_per_wave;

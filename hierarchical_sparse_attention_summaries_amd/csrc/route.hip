@@ -21,6 +21,7 @@
 // chunks can be selected, so the routed sets are those of the two-level rule.
 #include "hga_device.h"
 #include "hga_internal.h"
+#include "hga_select.h"
 
 namespace hga {
 namespace {
@@ -29,98 +30,17 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;  // one query row per wave in the selection
 constexpr int kMaxRows = 16;
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Selection for one query row, run by one whole wave.
-template <int E>
-__device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
-  const int lane = lane_id();
-  const int L = p / a.C;  // the query's own chunk
-  const float* cs = a.chunk_scores + static_cast<size_t>(row) * a.n_c;
-  const float* gs = a.group_scores + static_cast<size_t>(row) * a.n_g;
-  int n_kept;
-  if (L + 1 <= a.k_c + 2) {
-    n_kept = L + 1;
-    for (int t = lane; t < n_kept; t += kWave) s_kept[t] = t;
-  } else {
-    n_kept = a.k_c + 2;
-    if (lane == 0) {
-      s_kept[0] = 0;
-      s_kept[n_kept - 1] = L;
-    }
-    if (a.k_c > 0) {
-      // candidates: chunks 1 .. L-1, item t <-> chunk 1 + t
-      uint32_t key[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int t = e * kWave + lane;
-        key[e] = t < L - 1 ? order_key(load_shared(cs + 1 + t)) : 0u;
-      }
-      const uint32_t chosen = wave_top_k<E>(key, a.k_c);
-      int before = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool c = (chosen >> e) & 1u;
-        const uint64_t m = ballot(c);
-        if (c) s_kept[1 + before + bits_below(m)] = 1 + e * kWave + lane;
-        before += __popcll(m);
-      }
-    }
-  }
-  wave_lds_sync();
-  if (a.chunk_idx) {
-    int32_t* out = a.chunk_idx + static_cast<size_t>(row) * (a.k_c + 2);
-    for (int t = lane; t < a.k_c + 2; t += kWave) out[t] = t < n_kept ? s_kept[t] : -1;
-  }
-  // candidate groups of the kept chunks, in ascending group order
-  const int n_items = n_kept * a.gpc;
-  uint32_t key[E];
-  int gid[E];
-  int n_valid = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int t = e * kWave + lane;
-    bool valid = false;
-    int g = -1;
-    if (t < n_items) {
-      g = s_kept[t / a.gpc] * a.gpc + t % a.gpc;
-      valid = g < a.n_g && static_cast<int64_t>(g) * a.G <= p;
-    }
-    gid[e] = g;
-    key[e] = valid ? order_key(load_shared(gs + g)) : 0u;
-    n_valid += __popcll(ballot(valid));
-  }
-  uint32_t chosen = 0;
-  if (n_valid <= a.k_g) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) chosen |= static_cast<uint32_t>(key[e] != 0u) << e;
-  } else {
-    chosen = wave_top_k<E>(key, a.k_g);
-  }
-  int32_t* out = a.group_idx + static_cast<size_t>(row) * a.k_g;
-  int before = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool c = (chosen >> e) & 1u;
-    const uint64_t m = ballot(c);
-    if (c) out[before + bits_below(m)] = gid[e];
-    before += __popcll(m);
-  }
-  for (int t = before + lane; t < a.k_g; t += kWave) out[t] = -1;
-  wave_lds_sync();  // s_kept is reused by this wave's next row
-}
-
 template <typename TQ, int D, int RM>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblocks,
                                                          int chunks_per_split, int n_splits,
-                                                         int e_sel) {
+                                                         int e_sel, int kept_cap) {
   constexpr int DPL = 8;          // summary dims per lane (two 16-byte fp32 loads)
   constexpr int LPR = D / DPL;    // lanes per summary row
   constexpr int RPS = kWave / LPR;
-  extern __shared__ int s_kept_all[];
+  // Dynamic LDS: first the score staging [RM][items] (phase 1), then, after
+  // the arrival barrier, the per-wave kept-chunk lists (selection).
+  extern __shared__ int s_dyn[];
+  float* s_stage = reinterpret_cast<float*>(s_dyn);
   __shared__ bool s_last;
 
   const int unit = blockIdx.x / n_splits;
@@ -206,52 +126,58 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (base0 + j * kStride >= n_items) break;  // wave-uniform
-      float* dst_base = is_chunk[j] ? a.chunk_scores : a.group_scores;
-      const int dst_stride = is_chunk[j] ? a.n_c : a.n_g;
+      const int item = base0 + j * kStride + sub;
 #pragma unroll
       for (int rho = 0; rho < RM; ++rho) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) d = fmaf(qr[rho][e], sv[j][e], d);
         d = group_sum<LPR>(d);
-        if (valid[j] && rho < rows_here && (lane % LPR) == (rho % LPR))
-          store_shared(dst_base + static_cast<size_t>(row_of(rho)) * dst_stride + dst_col[j], d);
+        if (valid[j] && (lane % LPR) == (rho % LPR)) s_stage[rho * n_items + item] = d;
       }
+    }
+  }
+  __syncthreads();
+  // Each query row's scores of this slice are contiguous in the workspace:
+  // chunk scores [c_lo, c_hi), group scores from c_lo * gpc. Write them out
+  // with consecutive lanes on consecutive columns.
+  {
+    const int n_grp = min(n_ch * a.gpc, a.n_g - c_lo * a.gpc);
+    const int per_row = n_ch + n_grp;
+    for (int idx = threadIdx.x; idx < rows_here * per_row; idx += kThreads) {
+      const int rho = idx / per_row;
+      const int it = idx % per_row;
+      const size_t row = static_cast<size_t>(row_of(rho));
+      float* dst = it < n_ch ? a.chunk_scores + row * a.n_c + c_lo + it
+                             : a.group_scores + row * a.n_g + c_lo * a.gpc + (it - n_ch);
+      store_shared(dst, s_stage[rho * n_items + it]);
     }
   }
 
   if (!arrive_last(a.counters + unit, static_cast<unsigned>(n_splits), &s_last)) return;
 
-  int* s_kept = s_kept_all + wave * (a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2);
+  int* s_kept = s_dyn + wave * kept_cap;
   for (int rho = wave; rho < rows_here; rho += kWaves) {
     const int row = row_of(rho);
     const int p = a.T - a.Nq + (qb * kMaxRows + rho) / r;
-    switch (e_sel) {
-      case 1: select_row<1>(a, row, p, s_kept); break;
-      case 2: select_row<2>(a, row, p, s_kept); break;
-      case 3: select_row<3>(a, row, p, s_kept); break;
-      case 4: select_row<4>(a, row, p, s_kept); break;
-      case 5: select_row<5>(a, row, p, s_kept); break;
-      case 6: select_row<6>(a, row, p, s_kept); break;
-      case 8: select_row<8>(a, row, p, s_kept); break;
-      case 16: select_row<16>(a, row, p, s_kept); break;
-      case 32: select_row<32>(a, row, p, s_kept); break;
-      default: select_row<64>(a, row, p, s_kept); break;
-    }
+    select_row_e(e_sel, a, row, p, s_kept);
   }
 }
 
 template <typename TQ, int D>
 hipError_t launch_rm(const RouteArgs& a, const RoutePlan& plan, int rm, int e_sel,
-                     size_t lds, hipStream_t stream) {
+                     int kept_cap, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv *
                                                 plan.n_qblocks * plan.n_splits);
+  const size_t stage = static_cast<size_t>(rm) * plan.chunks_per_split * (1 + a.gpc) * sizeof(float);
+  const size_t kept = static_cast<size_t>(kWaves) * kept_cap * sizeof(int);
+  const size_t lds = stage > kept ? stage : kept;
   if (rm == 8) {
     hipLaunchKernelGGL((route_kernel<TQ, D, 8>), dim3(blocks), dim3(kThreads), lds, stream, a,
-                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel);
+                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap);
   } else {
     hipLaunchKernelGGL((route_kernel<TQ, D, 16>), dim3(blocks), dim3(kThreads), lds, stream, a,
-                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel);
+                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap);
   }
   return hipGetLastError();
 }
@@ -270,12 +196,18 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   const int64_t n_g = (T + G - 1) / G;
   pl.q_per_block = kMaxRows;
   pl.n_qblocks = static_cast<int>((r * Nq + kMaxRows - 1) / kMaxRows);
-  // Few workgroups per arrival counter (they bump it one after another), but
-  // at most 16 chunks (16 * (1 + chunk/group) summary rows) per workgroup.
+  // About one round of workgroups over the chip (a later round would wait for
+  // a whole earlier one, and the selection runs after the last), few
+  // workgroups per arrival counter (they bump it one after another), and at
+  // most 768 summary rows per workgroup (their scores for 16 query rows are
+  // staged in 48 KiB of LDS).
   const int64_t units = B * Hkv * pl.n_qblocks;
-  const int64_t target = static_cast<int64_t>(device_cu_count()) / 2;
+  const int64_t target = static_cast<int64_t>(device_cu_count());
   int64_t splits = (target + units - 1) / units;
-  const int64_t min_splits = (n_c + 15) / 16;
+  const int64_t gpc = C / G;
+  int64_t max_cps = 768 / (1 + gpc);
+  if (max_cps < 1) max_cps = 1;
+  const int64_t min_splits = (n_c + max_cps - 1) / max_cps;
   if (splits < min_splits) splits = min_splits;
   if (splits < 1) splits = 1;
   if (splits > n_c) splits = n_c;
@@ -286,6 +218,11 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   pl.off_chunk_scores = align_up(static_cast<size_t>(units) * sizeof(unsigned), 256);
   pl.off_group_scores = align_up(pl.off_chunk_scores + static_cast<size_t>(rows * n_c) * 4, 256);
   pl.bytes = align_up(pl.off_group_scores + static_cast<size_t>(rows * n_g) * 4, 256);
+  pl.off_split = 0;
+  if (r * Nq >= 64) {  // many query rows per KV head: room for the MFMA operand copies
+    pl.off_split = pl.bytes;
+    pl.bytes = align_up(pl.off_split + static_cast<size_t>(B * Hkv * (n_c + n_g) * 128) * 4, 256);
+  }
   return pl;
 }
 
@@ -293,24 +230,13 @@ hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hi
   const int r = a.Hq / a.Hkv;
   const int max_rows = r * a.Nq < kMaxRows ? r * a.Nq : kMaxRows;
   const int rm = max_rows <= 8 ? 8 : 16;
-  const int kept = a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2;
-  const int items = (a.n_c - 2 > kept * a.gpc) ? a.n_c - 2 : kept * a.gpc;
-  // registers per lane for the selection keys: the smallest variant that fits
-  const int need = (items + kWave - 1) / kWave;
-  int e_sel = 64;
-  for (int e : {1, 2, 3, 4, 5, 6, 8, 16, 32, 64}) {
-    if (e >= need) {
-      e_sel = e;
-      break;
-    }
-  }
-  const int kept_per_wave = a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2;
-  const size_t lds = static_cast<size_t>(kWaves) * kept_per_wave * sizeof(int);
+  const int e_sel = select_regs(a);
+  const int kept_cap = kept_capacity(a);
   if (dtype == kF32)
-    return a.D == 64 ? launch_rm<float, 64>(a, plan, rm, e_sel, lds, stream)
-                     : launch_rm<float, 128>(a, plan, rm, e_sel, lds, stream);
-  return a.D == 64 ? launch_rm<uint16_t, 64>(a, plan, rm, e_sel, lds, stream)
-                   : launch_rm<uint16_t, 128>(a, plan, rm, e_sel, lds, stream);
+    return a.D == 64 ? launch_rm<float, 64>(a, plan, rm, e_sel, kept_cap, stream)
+                     : launch_rm<float, 128>(a, plan, rm, e_sel, kept_cap, stream);
+  return a.D == 64 ? launch_rm<uint16_t, 64>(a, plan, rm, e_sel, kept_cap, stream)
+                   : launch_rm<uint16_t, 128>(a, plan, rm, e_sel, kept_cap, stream);
 }
 
 }  // namespace hga

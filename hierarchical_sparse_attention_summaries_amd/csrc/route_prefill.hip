@@ -1,0 +1,248 @@
+// Step 2 of HGA (abstract of "Hierarchical Global Attention (HGA)", arXiv
+// 2606.30709) for many queries at once (chunked prefill): scoring every query
+// row against the chunk and group summaries is a dense contraction
+// Q[rows x D] x S^T[D x (n_chunks + n_groups)] per KV head, run on MFMA; the
+// selection then runs one wave per query row.
+//
+// Precision: Q holds bf16 values (exact as bf16 MFMA operands); each fp32
+// summary s is split into bf16 s_hi = rne(s) and s_lo = rne(s - s_hi), and the
+// score is q.s_hi + q.s_lo with fp32 accumulation. Products of bf16 values are
+// exact in fp32, and s_hi + s_lo carries s to about 2^-17 relative, so the
+// scores match an fp32 dot product to ~1e-6 relative: far inside the 1e-3 score
+// margin within which routed sets must agree exactly.
+//
+// Kernel 1 (split): every summary row becomes bf16 (hi, lo) rows once, in the
+// MFMA operand layout. Kernel 2 (scores): a workgroup of 4 waves owns 64 query
+// rows and walks all columns in 128-column tiles; each wave a 32 x 64 block per
+// tile = 2 x 4 MFMA 16x16x32 tiles over D/32 k-steps, two MFMAs (hi, lo) per
+// step, the next 16-column block's operands loading meanwhile. Query rows are
+// taken head-major (row = head-in-group * Nq + query), so a tile's rows are 64
+// consecutive workspace rows; the tile is staged in LDS and written out as
+// full contiguous row segments. Kernel 3 (select): one wave per query row,
+// the shared selection code.
+#include "hga_device.h"
+#include "hga_internal.h"
+#include "hga_select.h"
+
+namespace hga {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kTileRows = 64;   // per workgroup
+constexpr int kTileCols = 128;  // per workgroup
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits, and the rounded value back in fp32.
+__device__ __forceinline__ uint32_t rne_bits(float f, float& back) {
+  const uint32_t b = bf16_bits(f);
+  back = __uint_as_float(b << 16);
+  return b;
+}
+
+// 8 fp32 -> (hi, lo) bf16x8 with hi + lo ~ x.
+__device__ __forceinline__ void split_hi_lo(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float b0, b1, c0, c1;
+    const uint32_t h0 = rne_bits(x[2 * i], b0);
+    const uint32_t h1 = rne_bits(x[2 * i + 1], b1);
+    const uint32_t l0 = rne_bits(x[2 * i] - b0, c0);
+    const uint32_t l1 = rne_bits(x[2 * i + 1] - b1, c1);
+    h[i] = h0 | (h1 << 16);
+    l[i] = l0 | (l1 << 16);
+  }
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// Summary rows (chunks, then groups) of one (sequence, KV head) -> bf16 hi/lo.
+template <int D>
+__global__ __launch_bounds__(kThreads) void split_kernel(RouteArgs a) {
+  const int N = a.n_c + a.n_g;
+  const int bkv = blockIdx.y;
+  const int idx8 = blockIdx.x * kThreads + threadIdx.x;  // one 8-dim piece per thread
+  if (idx8 >= N * (D / 8)) return;
+  const int n = idx8 / (D / 8);
+  const int d0 = (idx8 % (D / 8)) * 8;
+  const float* src = n < a.n_c ? a.chunk_mean + (static_cast<size_t>(bkv) * a.n_c + n) * D
+                               : a.group_mean + (static_cast<size_t>(bkv) * a.n_g + n - a.n_c) * D;
+  const float4 v0 = *reinterpret_cast<const float4*>(src + d0);
+  const float4 v1 = *reinterpret_cast<const float4*>(src + d0 + 4);
+  const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  bf16x8 hi, lo;
+  split_hi_lo(x, hi, lo);
+  uint16_t* base = a.split + static_cast<size_t>(bkv) * 2 * N * D;
+  *reinterpret_cast<bf16x8*>(base + static_cast<size_t>(n) * D + d0) = hi;
+  *reinterpret_cast<bf16x8*>(base + (static_cast<size_t>(N) + n) * D + d0) = lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_mfma_kernel(RouteArgs a, int n_row_tiles,
+                                                              int n_col_tiles) {
+  constexpr int KS = D / 32;  // k-steps of the 16x16x32 MFMA
+  __shared__ float s_out[kTileRows][kTileCols + 4];  // +4: rows stay 16-byte aligned
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int lr = lane % 16;   // A: row in block; B: column in tile; D: column
+  const int lk = lane / 16;   // k sub-block (8 values); D: row quad
+  const int rt = blockIdx.x % n_row_tiles;
+  const int bkv = blockIdx.x / n_row_tiles;
+  const int kv = bkv % a.Hkv;
+  const int b = bkv / a.Hkv;
+  const int r = a.Hq / a.Hkv;
+  const int M = r * a.Nq;               // query rows of this (b, kv head), head-major
+  const int N = a.n_c + a.n_g;          // summary rows: chunks, then groups
+  const size_t row0 = static_cast<size_t>(b * a.Hq + kv * r) * a.Nq;  // workspace row of rho = 0
+  const int wr = (wave / 2) * 32;
+  const int wc = (wave % 2) * 64;
+  const int row_base = rt * kTileRows + wr;
+  const int nrows = min(kTileRows, M - rt * kTileRows);
+
+  // This wave's 32 query rows stay in registers for every column tile.
+  uint4 qa[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int rho = row_base + rb * 16 + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[rb][ks] = rho < M ? ld16(static_cast<const uint16_t*>(a.Q) + (row0 + rho) * D + ks * 32 +
+                                  lk * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const uint16_t* hi_base = a.split + static_cast<size_t>(bkv) * 2 * N * D;
+  const uint16_t* lo_base = hi_base + static_cast<size_t>(N) * D;
+
+  // B fragments of one 16-column block: KS k-steps of (hi, lo).
+  auto load_b = [&](int col, uint4 (&h)[KS], uint4 (&l)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (col < N) {
+        h[ks] = ld16(hi_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
+        l[ks] = ld16(lo_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
+      } else {
+        h[ks] = make_uint4(0, 0, 0, 0);
+        l[ks] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  for (int ct = 0; ct < n_col_tiles; ++ct) {
+    const int col_base = ct * kTileCols + wc;
+    uint4 hA[KS], lA[KS], hB[KS], lB[KS];
+    load_b(col_base + lr, hA, lA);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      // next block's fragments in flight while this one runs on MFMA
+      if (cb + 1 < 4) load_b(col_base + (cb + 1) * 16 + lr, (cb & 1) ? hA : hB, (cb & 1) ? lA : lB);
+      const uint4(&h)[KS] = (cb & 1) ? hB : hA;
+      const uint4(&l)[KS] = (cb & 1) ? lB : lA;
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][ks]), as_bf16x8(h[ks]),
+                                                            acc[rb], 0, 0, 0);
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][ks]), as_bf16x8(l[ks]),
+                                                            acc[rb], 0, 0, 0);
+        }
+      }
+      // D fragment: lane holds rows lk*4 + i of each 16-row block, column lr.
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_out[wr + rb * 16 + lk * 4 + i][wc + cb * 16 + lr] = acc[rb][i] * a.scale;
+    }
+    __syncthreads();
+    // The tile's rows, each a contiguous run of chunk or group columns in its
+    // workspace row: one wave per row, four columns per lane, 16-byte stores
+    // where the destination allows.
+    const int tile_col0 = ct * kTileCols;
+    const int ncols = min(kTileCols, N - tile_col0);
+    for (int tr = wave; tr < nrows; tr += kThreads / kWave) {
+      const size_t wrow = row0 + rt * kTileRows + tr;
+      for (int tc = lane * 4; tc < ncols; tc += kWave * 4) {
+        const int col = tile_col0 + tc;
+        const float4 v = *reinterpret_cast<const float4*>(&s_out[tr][tc]);
+        float* dst = col < a.n_c ? a.chunk_scores + wrow * a.n_c + col
+                                 : a.group_scores + wrow * a.n_g + (col - a.n_c);
+        const bool same_part = (col < a.n_c) == (col + 3 < a.n_c);
+        if (tc + 4 <= ncols && same_part && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+          for (int e = 0; e < 4 && tc + e < ncols; ++e) {
+            const int c = col + e;
+            if (c < a.n_c) {
+              a.chunk_scores[wrow * a.n_c + c] = vv[e];
+            } else {
+              a.group_scores[wrow * a.n_g + (c - a.n_c)] = vv[e];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // s_out is rewritten by the next tile
+  }
+}
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(RouteArgs a, int e_sel, int kept_cap) {
+  extern __shared__ int s_kept_all[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int row = blockIdx.x * kSelWaves + wave;
+  const int rows = a.B * a.Hq * a.Nq;
+  if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
+  const int i = row % a.Nq;
+  select_row_e(e_sel, a, row, a.T - a.Nq + i, s_kept_all + wave * kept_cap);
+}
+
+}  // namespace
+
+bool use_prefill_route(int dtype, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D) {
+  (void)D;
+  return dtype == kBF16 && (Hq / Hkv) * Nq >= 64;
+}
+
+hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream) {
+  const int r = a.Hq / a.Hkv;
+  const int M = r * a.Nq;
+  const int N = a.n_c + a.n_g;
+  const dim3 split_grid((N * (a.D / 8) + kThreads - 1) / kThreads, a.B * a.Hkv);
+  if (a.D == 64) {
+    hipLaunchKernelGGL((split_kernel<64>), split_grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((split_kernel<128>), split_grid, dim3(kThreads), 0, stream, a);
+  }
+  const int n_row_tiles = (M + kTileRows - 1) / kTileRows;
+  const int n_col_tiles = (N + kTileCols - 1) / kTileCols;
+  const int64_t blocks = static_cast<int64_t>(a.B) * a.Hkv * n_row_tiles;
+  if (a.D == 64) {
+    hipLaunchKernelGGL((score_mfma_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, stream, a, n_row_tiles, n_col_tiles);
+  } else {
+    hipLaunchKernelGGL((score_mfma_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, stream, a, n_row_tiles, n_col_tiles);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = a.B * a.Hq * a.Nq;
+  const int kept_cap = kept_capacity(a);
+  const size_t lds = static_cast<size_t>(kSelWaves) * kept_cap * sizeof(int);
+  hipLaunchKernelGGL(select_kernel, dim3((rows + kSelWaves - 1) / kSelWaves), dim3(kSelThreads), lds,
+                     stream, a, select_regs(a), kept_cap);
+  return hipGetLastError();
+}
+
+}  // namespace hga

@@ -94,7 +94,7 @@ int hga_summary_counts(int64_t seq_len, int32_t chunk, int32_t group,
  *   chunk_mean [B, Hkv, ceil(T/chunk), D] f32, written: mean key of each chunk.
  *   group_mean [B, Hkv, ceil(T/group), D] f32, written: mean key of each group.
  * A short last group or chunk is the mean of the keys it has. Accumulation is
- * fp32. chunk % group == 0; chunk / group <= 4096; group <= 65536.
+ * fp32. chunk % group == 0; chunk / group <= 512; group <= 65536.
  */
 int hga_build_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
                         int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,

@@ -28,6 +28,7 @@ class Workload:
     dtype: str      # "f32" or "bf16": type of Q, K, V
     plants: int     # planted q-aligned chunks per query head (0 = none)
     cosine: float = 0.6
+    host_kv: bool = False   # full K/V kept in pinned host memory (only summaries in HBM)
 
     @property
     def r(self) -> int:
@@ -63,6 +64,6 @@ SWEEP = {T: _decode(T, 16, f"qwen3-30b-a3b-decode-b16-t{T}")
 PREFILL = Workload(name="qwen3-30b-a3b-prefill-nq4096-t65536", B=1, Hq=32, Hkv=4, D=128,
                    T=65536, Nq=4096, chunk=256, group=32, k_chunk=32, k_group=64,
                    theta=1e6, dtype="bf16", plants=8)
-HOST_TIER = _decode(262144, 4, "qwen3-30b-a3b-host-tier-b4-t262144")
+HOST_TIER = _decode(262144, 4, "qwen3-30b-a3b-host-tier-b4-t262144").with_(host_kv=True)
 
 ALL = {w.name: w for w in [TINY, TINY_ALL, DECODE_64K, *SWEEP.values(), PREFILL, HOST_TIER]}

@@ -46,9 +46,10 @@ def check_summaries(cm_gpu, gm_gpu, cm_ref, gm_ref):
 
 
 def check_routes(Q, cm_ref, gm_ref, T, chunk, group, k_chunk, k_group, chunk_idx, group_idx,
-                 records, scale=None, b_list=None) -> RouteStats:
+                 records, scale=None, b_list=None, rows=None) -> RouteStats:
     """Q [B,Hq,Nq,D] (oracle dtype values); chunk_idx/group_idx from the GPU for the
-    same B; cm_ref/gm_ref the oracle's summaries for the sequences in b_list."""
+    same B; cm_ref/gm_ref the oracle's summaries for the sequences in b_list.
+    `rows`, if given, restricts the check to those (b, h, i) query rows."""
     B, Hq, Nq, _ = Q.shape
     Hkv = cm_ref.shape[1]
     r = Hq // Hkv
@@ -56,54 +57,56 @@ def check_routes(Q, cm_ref, gm_ref, T, chunk, group, k_chunk, k_group, chunk_idx
     n_g = gm_ref.shape[2]
     st = RouteStats()
     b_list = list(range(B)) if b_list is None else b_list
-    for bi, b in enumerate(b_list):
-        for h in range(Hq):
-            for i in range(Nq):
-                st.queries += 1
-                rq = records[(b, h, i)]
-                p = T - Nq + i
-                L = p // chunk
-                q = Q[b, h, i]
-                gc = [int(c) for c in chunk_idx[b, h, i] if c >= 0] if chunk_idx is not None else None
-                gg = [int(g) for g in group_idx[b, h, i] if g >= 0]
-                tag = (b, h, i)
-                # -- chunk level
-                if gc is not None:
-                    if rq.chunk_gap > MARGIN:
-                        if gc != rq.chunks:
-                            st.failures.append((tag, "chunk set", gc, rq.chunks))
-                    else:
-                        st.chunk_exempt += 1
-                    want_n = min(L + 1, k_chunk + 2)
-                    if len(gc) != want_n or gc != sorted(set(gc)) or gc[0] != 0 or gc[-1] != L:
-                        st.failures.append((tag, "chunk shape/forced", gc))
-                    else:
-                        mid_kept = [c for c in gc if 0 < c < L]
-                        mid_drop = [c for c in range(1, L) if c not in set(gc)]
-                        if mid_kept and mid_drop:
-                            s = rq.chunk_scores
-                            if min(s[c] for c in mid_kept) < max(s[c] for c in mid_drop) - MARGIN:
-                                st.failures.append((tag, "chunk not eps-valid"))
-                else:
-                    gc = rq.chunks
-                # -- group level
-                exact = rq.chunk_gap > MARGIN and rq.group_gap > MARGIN
-                if exact:
-                    if gg != rq.groups:
-                        st.failures.append((tag, "group set", gg, rq.groups))
-                else:
-                    st.group_exempt += 1
-                cands = [g for c in gc for g in range(c * gpc, (c + 1) * gpc)
-                         if g < n_g and g * group <= p]
-                if len(gg) != min(k_group, len(cands)) or gg != sorted(set(gg)) \
-                        or not set(gg) <= set(cands):
-                    st.failures.append((tag, "group shape/candidates", gg))
-                    continue
-                drop = [g for g in cands if g not in set(gg)]
-                if gg and drop:
-                    sc = oracle.score(q, gm_ref[bi, h // r][gg + drop], scale)
-                    if sc[:len(gg)].min() < sc[len(gg):].max() - MARGIN:
-                        st.failures.append((tag, "group not eps-valid"))
+    if rows is None:
+        rows = [(b, h, i) for b in b_list for h in range(Hq) for i in range(Nq)]
+    b_pos = {b: bi for bi, b in enumerate(b_list)}
+    for (b, h, i) in rows:
+        bi = b_pos[b]
+        st.queries += 1
+        rq = records[(b, h, i)]
+        p = T - Nq + i
+        L = p // chunk
+        q = Q[b, h, i]
+        gc = [int(c) for c in chunk_idx[b, h, i] if c >= 0] if chunk_idx is not None else None
+        gg = [int(g) for g in group_idx[b, h, i] if g >= 0]
+        tag = (b, h, i)
+        # -- chunk level
+        if gc is not None:
+            if rq.chunk_gap > MARGIN:
+                if gc != rq.chunks:
+                    st.failures.append((tag, "chunk set", gc, rq.chunks))
+            else:
+                st.chunk_exempt += 1
+            want_n = min(L + 1, k_chunk + 2)
+            if len(gc) != want_n or gc != sorted(set(gc)) or gc[0] != 0 or gc[-1] != L:
+                st.failures.append((tag, "chunk shape/forced", gc))
+            else:
+                mid_kept = [c for c in gc if 0 < c < L]
+                mid_drop = [c for c in range(1, L) if c not in set(gc)]
+                if mid_kept and mid_drop:
+                    s = rq.chunk_scores
+                    if min(s[c] for c in mid_kept) < max(s[c] for c in mid_drop) - MARGIN:
+                        st.failures.append((tag, "chunk not eps-valid"))
+        else:
+            gc = rq.chunks
+        # -- group level
+        exact = rq.chunk_gap > MARGIN and rq.group_gap > MARGIN
+        if exact:
+            if gg != rq.groups:
+                st.failures.append((tag, "group set", gg, rq.groups))
+        else:
+            st.group_exempt += 1
+        cands = [g for c in gc for g in range(c * gpc, (c + 1) * gpc)
+                 if g < n_g and g * group <= p]
+        if len(gg) != min(k_group, len(cands)) or gg != sorted(set(gg)) \
+                or not set(gg) <= set(cands):
+            st.failures.append((tag, "group shape/candidates", gg))
+            continue
+        drop = [g for g in cands if g not in set(gg)]
+        if gg and drop:
+            sc = oracle.score(q, gm_ref[bi, h // r][gg + drop], scale)
+            if sc[:len(gg)].min() < sc[len(gg):].max() - MARGIN:
+                st.failures.append((tag, "group not eps-valid"))
     return st
 
 

@@ -11,9 +11,9 @@ import torch
 
 import hierarchical_sparse_attention_summaries_amd as hga
 import oracle
-from synth import DECODE_64K, SWEEP, TINY, TINY_ALL, Workload, generate
+from synth import DECODE_64K, HOST_TIER, PREFILL, SWEEP, TINY, TINY_ALL, Workload, generate
 from tests import parity
-from tests.gpu_runner import check_workload, log, np_of, run_hip, to_dev
+from tests.gpu_runner import check_sampled, check_workload, log, np_of, run_hip, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,46 @@ EDGE = [
     # groups of 48 tokens (a partial second tile)
     Workload("edge-g48", 1, 4, 2, 128, 3000, 2, 96, 48, 5, 7, 1e4, "bf16", 0),
 ]
+
+
+# Many query rows per KV head (r * Nq >= 64, bf16): MFMA scoring + select kernel.
+PREFILL_SMALL = [
+    Workload("prefill-small", 1, 8, 2, 128, 4096, 100, 128, 32, 4, 8, 1e6, "bf16", 2),
+    Workload("prefill-d64-ragged", 2, 4, 1, 64, 2000, 64, 64, 16, 6, 10, 1e4, "bf16", 0),
+    Workload("prefill-gpc1-mha", 1, 2, 2, 128, 1500, 70, 32, 32, 5, 5, 1e4, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_SMALL, ids=lambda w: w.name)
+def test_prefill_small(w):
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+
+
+def test_prefill_4096_on_61440_sampled():
+    w = PREFILL
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_sampled(w, inp, out, n_rows=256)
+    # the last new token of every head retrieves its planted chunks
+    gidx = out["gidx"].cpu().numpy()
+    per = w.chunk // w.group
+    for h in range(w.Hq):
+        assert sorted(set(g // per for g in gidx[0, h, -1])) == inp.planted[(0, h)]
+
+
+def test_host_tier_b4_t262144_sampled():
+    """Full K/V in pinned host memory, summaries in HBM: the routed groups are
+    read over the host link. 256 sampled query rows against the oracle."""
+    w = HOST_TIER
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    assert not out["K"].is_cuda and out["cm"].is_cuda
+    check_sampled(w, inp, out, n_rows=128)
 
 
 @pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
@@ -172,3 +212,24 @@ def test_back_to_back_calls_share_workspace():
     check_workload(w, b, outs[1])
     check_workload(w, a, outs[2])
     assert torch.equal(outs[0]["O"], outs[2]["O"])
+
+
+def test_quality_proxy_matches_oracle():
+    """Share of the dense softmax mass on the routed tokens, from the library's
+    attention over all groups vs over the routed groups, against the oracle's
+    dense and routed log-sum-exp."""
+    log("case quality-proxy")
+    w = DECODE_64K.with_(T=16384, k_chunk=8, k_group=16, B=2)
+    inp = generate(w)
+    out = run_hip(w, inp)
+    all_g = torch.arange(w.n_groups, dtype=torch.int32, device="cuda")
+    all_g = all_g.expand(w.B, w.Hq, w.Nq, w.n_groups).contiguous()
+    Od, lsed = hga.attend(out["Q"], out["K"], out["V"], all_g, w.group)
+    torch.cuda.synchronize()
+    mass_gpu = torch.exp(out["lse"] - lsed).cpu().numpy()
+    Od_ref, lsed_ref = oracle.dense_causal(inp.Q, inp.K, inp.V)
+    parity.check_outputs(np_of(Od), lsed.cpu().numpy(), Od_ref, lsed_ref, w.dtype)
+    _, lser_ref = oracle.attend(inp.Q, inp.K, inp.V, out["gidx"].cpu().numpy(), w.group)
+    mass_ref = np.exp(lser_ref - lsed_ref)
+    assert np.abs(mass_gpu - mass_ref).max() < 2e-3 * max(1.0, mass_ref.max())
+    assert (mass_ref > 0).all() and (mass_ref <= 1 + 1e-9).all()   # a share of the dense mass
