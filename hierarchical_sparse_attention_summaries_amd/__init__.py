@@ -19,6 +19,7 @@ import torch
 
 __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summaries",
            "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
+           "Layout", "build_summaries_ex", "update_summaries_ex", "route_ex", "attend_ex",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
@@ -42,6 +43,37 @@ class Shape(ctypes.Structure):
                 ("seq_len", ctypes.c_int64), ("head_dim", ctypes.c_int64)]
 
 
+class _KvLayoutC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+class Layout:
+    """Ragged and/or paged K/V. seq_lens: int32 [B] device tensor of keys per
+    sequence (None: every sequence holds the full capacity). block_table: int32
+    [B, max_pages] device tensor of page ids (None: dense [B, Hkv, T, D] K/V);
+    with pages, K and V are pools [n_pages, Hkv, page_tokens, D]."""
+
+    def __init__(self, seq_lens=None, block_table=None, page_tokens=0, n_pages=0):
+        for t, n in ((seq_lens, "seq_lens"), (block_table, "block_table")):
+            if t is not None and (not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+        self.seq_lens, self.block_table = seq_lens, block_table
+        self.page_tokens, self.n_pages = page_tokens, n_pages
+
+    @property
+    def paged(self):
+        return self.block_table is not None
+
+    def c(self):
+        bt = self.block_table
+        return _KvLayoutC(1 if self.paged else 0, self.page_tokens,
+                          bt.shape[1] if self.paged else 0, self.n_pages,
+                          bt.data_ptr() if self.paged else None,
+                          self.seq_lens.data_ptr() if self.seq_lens is not None else None)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libhga.so not built at {LIB_PATH}; run "
@@ -63,6 +95,14 @@ def _load():
         "hga_attend_workspace_size": (ctypes.c_int, [P(Shape), i32, i32, P(sz)]),
         "hga_attend": (ctypes.c_int, [P(Shape), vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, vp,
                                       sz, vp]),
+        "hga_build_summaries_ex": (ctypes.c_int, [vp, i32, P(_KvLayoutC), i64, i64, i64, i64, i32,
+                                                  i32, vp, vp, vp]),
+        "hga_update_summaries_ex": (ctypes.c_int, [vp, i32, P(_KvLayoutC), i64, i64, i64, i64, i32,
+                                                   i32, i64, vp, vp, vp]),
+        "hga_route_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, i32, vp, vp, i32, i32, i32, i32,
+                                        f32, vp, vp, vp, sz, vp]),
+        "hga_attend_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, i32, i32, f32,
+                                         vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -250,4 +290,95 @@ def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, group_idx: torch.T
                            _ptr(group_idx), k_group, group, float(scale), _ptr(out),
                            _ptr(lse if want_lse else None), _ptr(ws), ws.numel(),
                            _stream(Q.device)), "hga_attend")
+    return out, (lse if want_lse else None)
+
+
+# ---------------------------------------------------------------- ragged / paged
+def _kv_dims(K, layout, batch, seq_len):
+    """(B, Hkv, T, D) of a dense cache or of a page pool under `layout`."""
+    if layout is not None and layout.paged:
+        _, H, page, D = K.shape
+        B = layout.block_table.shape[0]
+        T = seq_len if seq_len is not None else layout.block_table.shape[1] * page
+        if page != layout.page_tokens:
+            raise ValueError("page pool's third dim must equal layout.page_tokens")
+        return B, H, T, D
+    B, H, T, D = K.shape
+    return B, H, T, D
+
+
+def _lay(layout):
+    return ctypes.byref(layout.c()) if layout is not None else None
+
+
+def build_summaries_ex(K, chunk, group, layout=None, seq_len=None, chunk_mean=None,
+                       group_mean=None):
+    """build_summaries over a ragged and/or paged cache (see Layout)."""
+    _need(K, "K", 4, host_ok=True)
+    B, H, T, D = _kv_dims(K, layout, None, seq_len)
+    n_c, n_g = summary_counts(T, chunk, group)
+    dev = _gpu_of(K)
+    if chunk_mean is None:
+        chunk_mean = torch.zeros((B, H, n_c, D), dtype=torch.float32, device=dev)
+    if group_mean is None:
+        group_mean = torch.zeros((B, H, n_g, D), dtype=torch.float32, device=dev)
+    _check(_lib.hga_build_summaries_ex(_ptr(K), _dtype_code(K), _lay(layout), B, H, T, D, chunk,
+                                       group, _ptr(chunk_mean), _ptr(group_mean), _stream(dev)),
+           "hga_build_summaries_ex")
+    return chunk_mean, group_mean
+
+
+def update_summaries_ex(K, chunk, group, newest, chunk_mean, group_mean, layout=None,
+                        seq_len=None):
+    """Refresh the chunks holding each sequence's newest `newest` keys."""
+    _need(K, "K", 4, host_ok=True)
+    B, H, T, D = _kv_dims(K, layout, None, seq_len)
+    _check(_lib.hga_update_summaries_ex(_ptr(K), _dtype_code(K), _lay(layout), B, H, T, D, chunk,
+                                        group, newest, _ptr(chunk_mean), _ptr(group_mean),
+                                        _stream(chunk_mean.device)), "hga_update_summaries_ex")
+
+
+def route_ex(Q, chunk_mean, group_mean, seq_len, chunk, group, k_chunk, k_group, layout=None,
+             scale=0.0, want_chunks=True, chunk_idx=None, group_idx=None, workspace=None):
+    """route with per-sequence lengths (layout.seq_lens); seq_len is the capacity T."""
+    _need(Q, "Q", 4)
+    B, Hq, Nq, D = Q.shape
+    Hkv = chunk_mean.shape[1]
+    shape = _shape(Q, Hkv, seq_len)
+    nbytes = route_workspace_bytes(shape, chunk, group, k_chunk, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "route", nbytes)
+    if want_chunks and chunk_idx is None:
+        chunk_idx = torch.empty((B, Hq, Nq, k_chunk + 2), dtype=torch.int32, device=Q.device)
+    if group_idx is None:
+        group_idx = torch.empty((B, Hq, Nq, k_group), dtype=torch.int32, device=Q.device)
+    _check(_lib.hga_route_ex(ctypes.byref(shape), _lay(layout), _ptr(Q), _dtype_code(Q),
+                             _ptr(chunk_mean), _ptr(group_mean), chunk, group, k_chunk, k_group,
+                             float(scale), _ptr(chunk_idx), _ptr(group_idx), _ptr(ws), ws.numel(),
+                             _stream(Q.device)), "hga_route_ex")
+    return chunk_idx, group_idx
+
+
+def attend_ex(Q, K, V, group_idx, group, layout=None, seq_len=None, scale=0.0, want_lse=True,
+              out=None, lse=None, workspace=None):
+    """attend over a ragged and/or paged cache (see Layout)."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    _need(V, "V", 4, host_ok=True)
+    _need(group_idx, "group_idx", 4)
+    B, Hq, Nq, D = Q.shape
+    Bk, Hkv, T, Dk = _kv_dims(K, layout, None, seq_len)
+    if (Bk, Dk) != (B, D) or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K/V do not match Q")
+    k_group = group_idx.shape[3]
+    shape = _shape(Q, Hkv, T)
+    nbytes = attend_workspace_bytes(shape, group, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "attend", nbytes)
+    if out is None:
+        out = torch.empty_like(Q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    _check(_lib.hga_attend_ex(ctypes.byref(shape), _lay(layout), _ptr(Q), _ptr(K), _ptr(V),
+                              _dtype_code(Q), _ptr(group_idx), k_group, group, float(scale),
+                              _ptr(out), _ptr(lse if want_lse else None), _ptr(ws), ws.numel(),
+                              _stream(Q.device)), "hga_attend_ex")
     return out, (lse if want_lse else None)

@@ -66,6 +66,27 @@ int check_route_params(const hga_shape* s, int32_t chunk, int32_t group, int32_t
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Checks a caller's K/V layout against the capacity T and group size and
+// converts it; NULL means dense with every sequence holding T keys.
+int to_layout(const hga_kv_layout* in, int64_t T, int32_t group, hga::KvLayout* out) {
+  *out = hga::KvLayout{};
+  if (!in) return HGA_OK;
+  out->seq_lens = in->seq_lens;
+  if (in->kind == HGA_KV_DENSE) return HGA_OK;
+  if (in->kind != HGA_KV_PAGED) return HGA_ERR_PARAM;
+  if (!in->block_table) return HGA_ERR_NULL;
+  if (in->page_tokens < 1 || group < 1 || in->page_tokens % group != 0 || in->n_pages < 1 ||
+      in->max_pages < 1)
+    return HGA_ERR_PARAM;
+  if (static_cast<int64_t>(in->max_pages) * in->page_tokens < T) return HGA_ERR_PARAM;
+  out->paged = 1;
+  out->page_tokens = in->page_tokens;
+  out->max_pages = in->max_pages;
+  out->n_pages = in->n_pages;
+  out->block_table = in->block_table;
+  return HGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,10 +117,10 @@ int hga_summary_counts(int64_t seq_len, int32_t chunk, int32_t group, int64_t* n
   return HGA_OK;
 }
 
-static int summaries_common(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
-                            int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
-                            int64_t t_begin, int64_t t_end, float* chunk_mean,
-                            float* group_mean, void* stream) {
+static int summaries_common(const void* K, int32_t dtype, const hga_kv_layout* layout,
+                            int64_t batch, int64_t kv_heads, int64_t seq_len, int64_t head_dim,
+                            int32_t chunk, int32_t group, int64_t t_begin, int64_t t_end,
+                            int64_t newest, float* chunk_mean, float* group_mean, void* stream) {
   if (!K || !chunk_mean || !group_mean) return HGA_ERR_NULL;
   if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
   if (batch < 1 || kv_heads < 1 || batch >= kMaxDim || kv_heads >= kMaxDim) return HGA_ERR_SHAPE;
@@ -107,31 +128,58 @@ static int summaries_common(const void* K, int32_t dtype, int64_t batch, int64_t
   int st = check_chunking(seq_len, chunk, group);
   if (st != HGA_OK) return st;
   if (batch * kv_heads * seq_len >= (int64_t(1) << 40)) return HGA_ERR_SHAPE;
-  if (t_begin < 0 || t_end > seq_len || t_begin >= t_end) return HGA_ERR_PARAM;
+  hga::KvLayout L;
+  st = to_layout(layout, seq_len, group, &L);
+  if (st != HGA_OK) return st;
   if (!aligned16(K) || !aligned16(chunk_mean) || !aligned16(group_mean)) return HGA_ERR_LAYOUT;
-  const int64_t c_begin = t_begin / chunk;
-  const int64_t c_end = (t_end + chunk - 1) / chunk;
-  if (batch * kv_heads * (c_end - c_begin) >= kMaxDim) return HGA_ERR_SHAPE;
-  const hipError_t e = hga::launch_summaries(K, dtype, batch * kv_heads, head_dim, seq_len, chunk,
-                                             group, static_cast<int>(c_begin),
-                                             static_cast<int>(c_end), chunk_mean, group_mean,
-                                             as_stream(stream));
+  const int64_t n_c = (seq_len + chunk - 1) / chunk;
+  int64_t c_begin = 0, n_chunks = n_c;
+  if (newest > 0) {
+    if (newest > seq_len) return HGA_ERR_PARAM;
+    n_chunks = std::min<int64_t>(n_c, (newest + chunk - 1) / chunk + 1);
+  } else {
+    if (t_begin < 0 || t_end > seq_len || t_begin >= t_end) return HGA_ERR_PARAM;
+    c_begin = t_begin / chunk;
+    n_chunks = (t_end + chunk - 1) / chunk - c_begin;
+  }
+  if (batch * kv_heads * n_chunks >= kMaxDim) return HGA_ERR_SHAPE;
+  const hipError_t e = hga::launch_summaries(K, dtype, L, batch, kv_heads, head_dim, seq_len,
+                                             chunk, group, static_cast<int>(c_begin),
+                                             static_cast<int>(n_chunks), newest, chunk_mean,
+                                             group_mean, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 
 int hga_build_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
                         int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
                         float* chunk_mean, float* group_mean, void* stream) {
-  return summaries_common(K, dtype, batch, kv_heads, seq_len, head_dim, chunk, group, 0, seq_len,
-                          chunk_mean, group_mean, stream);
+  return summaries_common(K, dtype, nullptr, batch, kv_heads, seq_len, head_dim, chunk, group, 0,
+                          seq_len, 0, chunk_mean, group_mean, stream);
 }
 
 int hga_update_summaries(const void* K, int32_t dtype, int64_t batch, int64_t kv_heads,
                          int64_t seq_len, int64_t head_dim, int32_t chunk, int32_t group,
                          int64_t t_begin, int64_t t_end, float* chunk_mean, float* group_mean,
                          void* stream) {
-  return summaries_common(K, dtype, batch, kv_heads, seq_len, head_dim, chunk, group, t_begin,
-                          t_end, chunk_mean, group_mean, stream);
+  return summaries_common(K, dtype, nullptr, batch, kv_heads, seq_len, head_dim, chunk, group,
+                          t_begin, t_end, 0, chunk_mean, group_mean, stream);
+}
+
+int hga_build_summaries_ex(const void* K, int32_t dtype, const hga_kv_layout* layout,
+                           int64_t batch, int64_t kv_heads, int64_t seq_len, int64_t head_dim,
+                           int32_t chunk, int32_t group, float* chunk_mean, float* group_mean,
+                           void* stream) {
+  return summaries_common(K, dtype, layout, batch, kv_heads, seq_len, head_dim, chunk, group, 0,
+                          seq_len, 0, chunk_mean, group_mean, stream);
+}
+
+int hga_update_summaries_ex(const void* K, int32_t dtype, const hga_kv_layout* layout,
+                            int64_t batch, int64_t kv_heads, int64_t seq_len, int64_t head_dim,
+                            int32_t chunk, int32_t group, int64_t newest, float* chunk_mean,
+                            float* group_mean, void* stream) {
+  if (newest < 1) return HGA_ERR_PARAM;
+  return summaries_common(K, dtype, layout, batch, kv_heads, seq_len, head_dim, chunk, group, 0,
+                          0, newest, chunk_mean, group_mean, stream);
 }
 
 int hga_route_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
@@ -151,8 +199,18 @@ int hga_route(const hga_shape* shape, const void* Q, int32_t dtype, const float*
               const float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
               int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
               void* workspace, size_t workspace_bytes, void* stream) {
+  return hga_route_ex(shape, nullptr, Q, dtype, chunk_mean, group_mean, chunk, group, k_chunk,
+                      k_group, scale, chunk_idx, group_idx, workspace, workspace_bytes, stream);
+}
+
+int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                 int32_t dtype, const float* chunk_mean, const float* group_mean, int32_t chunk,
+                 int32_t group, int32_t k_chunk, int32_t k_group, float scale,
+                 int32_t* chunk_idx, int32_t* group_idx, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != HGA_OK) return st;
+  if (layout && layout->kind != HGA_KV_DENSE && layout->kind != HGA_KV_PAGED) return HGA_ERR_PARAM;
   if (!Q || !chunk_mean || !group_mean || !group_idx || !workspace) return HGA_ERR_NULL;
   if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
   st = check_route_params(shape, chunk, group, k_chunk, k_group);
@@ -188,6 +246,7 @@ int hga_route(const hga_shape* shape, const void* Q, int32_t dtype, const float*
   a.chunk_scores = reinterpret_cast<float*>(ws + plan.off_chunk_scores);
   a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
   a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
+  a.seq_lens = layout ? layout->seq_lens : nullptr;
   const hipError_t e =
       (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
                                          shape->n_queries, shape->head_dim))
@@ -211,11 +270,22 @@ int hga_attend(const hga_shape* shape, const void* Q, const void* K, const void*
                int32_t dtype, const int32_t* group_idx, int32_t k_group, int32_t group,
                float scale, void* O, float* lse, void* workspace, size_t workspace_bytes,
                void* stream) {
+  return hga_attend_ex(shape, nullptr, Q, K, V, dtype, group_idx, k_group, group, scale, O, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                  const void* K, const void* V, int32_t dtype, const int32_t* group_idx,
+                  int32_t k_group, int32_t group, float scale, void* O, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !group_idx || !O || !workspace) return HGA_ERR_NULL;
   if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
   if (group < 1 || group > 65536 || k_group < 1) return HGA_ERR_PARAM;
+  hga::KvLayout L;
+  st = to_layout(layout, shape->seq_len, group, &L);
+  if (st != HGA_OK) return st;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
     return HGA_ERR_LAYOUT;
   const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
@@ -241,6 +311,7 @@ int hga_attend(const hga_shape* shape, const void* Q, const void* K, const void*
   char* ws = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
   a.partials = reinterpret_cast<float*>(ws + plan.off_partials);
+  a.kv = L;
   const hipError_t e = hga::launch_attend(a, dtype, plan, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }

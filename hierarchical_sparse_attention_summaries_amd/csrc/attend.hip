@@ -45,15 +45,15 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kv = h / (a.Hq / a.Hkv);
-  const int p = a.T - a.Nq + i;
-  const int t_lim = p + 1;  // tokens j <= p (and j < T since p < T)
+  const int p = seq_len_of(a.kv, b, a.T) - a.Nq + i;
+  const int t_lim = p + 1;  // tokens j <= p (p < the sequence's length <= T); none if p < 0
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int sub = lane / LPR;
   const int col = (lane % LPR) * EPL;
 
-  const TKV* Kb = static_cast<const TKV*>(a.K) + static_cast<size_t>(b * a.Hkv + kv) * a.T * D;
-  const TKV* Vb = static_cast<const TKV*>(a.V) + static_cast<size_t>(b * a.Hkv + kv) * a.T * D;
+  const TKV* Kbase = static_cast<const TKV*>(a.K);
+  const TKV* Vbase = static_cast<const TKV*>(a.V);
 
   float q[EPL];
   {
@@ -74,25 +74,30 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
   const int n_g = (a.T + a.G - 1) / a.G;
 
   // Token range [t0, t1) of list entry e (empty for -1 padding, ids out of
-  // range, and groups that start after the query).
-  auto span = [&](int e, int& t0, int& t1) {
+  // range, groups that start after the query, and pages out of range), and the
+  // element offset of its first row: the group's rows are consecutive.
+  auto span = [&](int e, int& t0, int& t1, int64_t& off) {
     const int g = e < e1 ? gl[e] : -1;
-    if (g < 0 || g >= n_g) {
-      t0 = t1 = 0;
-      return;
-    }
-    t0 = g * a.G;
-    t1 = min(t0 + a.G, t_lim);
-    if (t1 < t0) t1 = t0;
+    t0 = t1 = 0;
+    off = 0;
+    if (g < 0 || g >= n_g) return;
+    const int s0 = g * a.G;
+    const int s1 = min(s0 + a.G, t_lim);
+    if (s1 <= s0) return;
+    off = kv_offset(a.kv, b, a.Hkv, kv, a.T, D, s0);
+    if (off < 0) return;
+    t0 = s0;
+    t1 = s1;
   };
   // Issue the loads of up to kTile tokens from `base` (rows >= t1 read as 0).
-  auto load = [&](int base, int t1, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+  auto load = [&](int base, int t1, int64_t off, int t0, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int t = base + u * RPL + sub;
       if (t < t1) {
-        kr[u] = ld16(Kb + static_cast<size_t>(t) * D + col);
-        vr[u] = ld16(Vb + static_cast<size_t>(t) * D + col);
+        const int64_t at = off + static_cast<int64_t>(t - t0) * D + col;  // row t of the group
+        kr[u] = ld16(Kbase + at);
+        vr[u] = ld16(Vbase + at);
       } else {
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
@@ -137,14 +142,15 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
     // values are in flight while the current one is folded in.
     uint4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
     int a0, a1, b0, b1;
-    span(e0, a0, a1);
-    load(a0, a1, kA, vA);
+    int64_t ao, bo;
+    span(e0, a0, a1, ao);
+    load(a0, a1, ao, a0, kA, vA);
     for (int e = e0; e < e1; e += 2) {
-      span(e + 1, b0, b1);
-      load(b0, b1, kB, vB);
+      span(e + 1, b0, b1, bo);
+      load(b0, b1, bo, b0, kB, vB);
       if (a0 < a1) consume(a0, a1, kA, vA);
-      span(e + 2, a0, a1);
-      load(a0, a1, kA, vA);
+      span(e + 2, a0, a1, ao);
+      load(a0, a1, ao, a0, kA, vA);
       if (b0 < b1) consume(b0, b1, kB, vB);
     }
   } else {
@@ -152,9 +158,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
     uint4 kA[NLD], vA[NLD];
     for (int e = e0; e < e1; ++e) {
       int t0, t1;
-      span(e, t0, t1);
+      int64_t off;
+      span(e, t0, t1, off);
       for (int base = t0; base < t1; base += kTile) {
-        load(base, t1, kA, vA);
+        load(base, t1, off, t0, kA, vA);
         consume(base, t1, kA, vA);
       }
     }

@@ -16,9 +16,41 @@ constexpr int kBF16 = 1;
 constexpr int kMaxSelectItems = 4096;
 constexpr int kMaxKeptChunks = 1024;
 
-hipError_t launch_summaries(const void* K, int dtype, int64_t BH, int64_t D, int64_t T,
-                            int C, int G, int c_begin, int c_end, float* chunk_mean,
-                            float* group_mean, hipStream_t stream);
+// Where the keys/values of token t of (sequence b, KV head kv) live, and how
+// many tokens each sequence holds.
+struct KvLayout {
+  int paged;                   // 0: [B, Hkv, T, D]; 1: pages [n_pages, Hkv, page_tokens, D]
+  int page_tokens;             // paged: tokens per page (a multiple of the group size)
+  int max_pages;               // paged: columns of block_table
+  int n_pages;                 // paged: pages in the pool (ids outside are skipped)
+  const int32_t* block_table;  // paged: [B, max_pages] page ids
+  const int32_t* seq_lens;     // [B] tokens per sequence (clamped to [0, T]), or null: all T
+};
+
+__device__ __forceinline__ int seq_len_of(const KvLayout& L, int b, int T) {
+  if (!L.seq_lens) return T;
+  const int t = L.seq_lens[b];
+  return t < 0 ? 0 : (t > T ? T : t);
+}
+
+// Element offset of token t of (b, kv), or -1 if its page id is out of range.
+// The G tokens of one group are consecutive rows from there (pages hold whole
+// groups).
+__device__ __forceinline__ int64_t kv_offset(const KvLayout& L, int b, int Hkv, int kv, int T,
+                                             int D, int t) {
+  if (!L.paged) return (static_cast<int64_t>(b * Hkv + kv) * T + t) * D;
+  const int page = L.block_table[static_cast<int64_t>(b) * L.max_pages + t / L.page_tokens];
+  if (page < 0 || page >= L.n_pages) return -1;
+  return ((static_cast<int64_t>(page) * Hkv + kv) * L.page_tokens + t % L.page_tokens) * D;
+}
+
+// Summaries of chunks [c_first_b, c_first_b + n_chunks) of every (b, kv), where
+// c_first_b = max(0, T_b - newest) / C when newest > 0 (the chunks holding each
+// sequence's newest `newest` tokens), else c_first_b = c_begin.
+hipError_t launch_summaries(const void* K, int dtype, const KvLayout& L, int64_t B, int64_t Hkv,
+                            int64_t D, int64_t T, int C, int G, int c_begin, int n_chunks,
+                            int64_t newest, float* chunk_mean, float* group_mean,
+                            hipStream_t stream);
 
 struct RoutePlan {
   int q_per_block;      // queries of one sequence scored together per KV head
@@ -46,6 +78,7 @@ struct RouteArgs {
   float* group_scores; // workspace [B*Hq*Nq, n_g]
   unsigned* counters;  // workspace [B*Hkv*n_qblocks]
   uint16_t* split;     // workspace [B*Hkv, 2, n_c + n_g, D] bf16 (hi, lo); prefill path only
+  const int32_t* seq_lens;  // [B] or null (all sequences hold T tokens)
 };
 hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hipStream_t stream);
 
@@ -73,6 +106,7 @@ struct AttendArgs {
   float scale;
   float* partials;     // workspace [rows, n_splits, D + 2]
   unsigned* counters;  // workspace [rows]
+  KvLayout kv;
 };
 hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
                          hipStream_t stream);

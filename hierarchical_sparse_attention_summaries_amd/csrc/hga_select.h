@@ -20,6 +20,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int E>
 __device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, int* s_kept) {
   const int lane = lane_id();
+  if (p < 0) {  // a query position before the sequence's first key: nothing to route
+    if (a.chunk_idx)
+      for (int t = lane; t < a.k_c + 2; t += kWave) a.chunk_idx[static_cast<size_t>(row) * (a.k_c + 2) + t] = -1;
+    for (int t = lane; t < a.k_g; t += kWave) a.group_idx[static_cast<size_t>(row) * a.k_g + t] = -1;
+    return;
+  }
   const int L = p / a.C;  // the query's own chunk
   const float* cs = a.chunk_scores + static_cast<size_t>(row) * a.n_c;
   const float* gs = a.group_scores + static_cast<size_t>(row) * a.n_g;
@@ -121,6 +127,13 @@ inline int select_regs(const RouteArgs& a) {
     if (e >= need) return e;
   }
   return 64;
+}
+
+// Keys of sequence b (all T unless per-sequence lengths are given).
+__device__ __forceinline__ int route_seq_len(const RouteArgs& a, int b) {
+  if (!a.seq_lens) return a.T;
+  const int t = a.seq_lens[b];
+  return t < 0 ? 0 : (t > a.T ? a.T : t);
 }
 
 // Chunk ids one query keeps at most (the per-wave LDS list length).

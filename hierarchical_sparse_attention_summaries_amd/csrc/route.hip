@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
   int* s_kept = s_dyn + wave * kept_cap;
   for (int rho = wave; rho < rows_here; rho += kWaves) {
     const int row = row_of(rho);
-    const int p = a.T - a.Nq + (qb * kMaxRows + rho) / r;
+    const int p = route_seq_len(a, b) - a.Nq + (qb * kMaxRows + rho) / r;
     select_row_e(e_sel, a, row, p, s_kept);
   }
 }

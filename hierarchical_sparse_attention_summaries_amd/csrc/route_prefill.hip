@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteArgs a, int e_
   const int rows = a.B * a.Hq * a.Nq;
   if (row >= rows) return;  // whole wave leaves; no workgroup barrier follows
   const int i = row % a.Nq;
-  select_row_e(e_sel, a, row, a.T - a.Nq + i, s_kept_all + wave * kept_cap);
+  const int b = row / (a.Hq * a.Nq);
+  select_row_e(e_sel, a, row, route_seq_len(a, b) - a.Nq + i, s_kept_all + wave * kept_cap);
 }
 
 }  // namespace

@@ -166,6 +166,64 @@ int hga_attend(const hga_shape* shape, const void* Q, const void* K, const void*
                float scale, void* O, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Ragged and paged K/V (batched serving).
+ *
+ * The same three steps over a batch whose sequences hold different numbers of
+ * keys, with K/V either dense [B, Hkv, T, D] (T = capacity) or in a pool of
+ * pages addressed through a block table. Sequence b holds seq_lens[b] keys
+ * (clamped to [0, T]); its Nq queries sit at positions seq_lens[b]-Nq ..
+ * seq_lens[b]-1 (queries at negative positions route to nothing: -1 indices,
+ * O = 0, lse = -inf). Summaries stay [B, Hkv, ceil(T/chunk), D]; entries past a
+ * sequence's last chunk are not written and never read by routing.
+ * ------------------------------------------------------------------------ */
+typedef enum hga_kv_kind {
+  HGA_KV_DENSE = 0,  /* K, V are [B, Hkv, T, D] */
+  HGA_KV_PAGED = 1   /* K, V are page pools [n_pages, Hkv, page_tokens, D] */
+} hga_kv_kind;
+
+typedef struct hga_kv_layout {
+  int32_t kind;                /* hga_kv_kind */
+  int32_t page_tokens;         /* paged: tokens per page, a multiple of `group` */
+  int32_t max_pages;           /* paged: columns of block_table, >= ceil(T / page_tokens) */
+  int32_t n_pages;             /* paged: pages in the pool; ids outside [0, n_pages) are
+                                  skipped (their tokens count as absent) */
+  const int32_t* block_table;  /* paged: [B, max_pages] int32 page ids, device memory;
+                                  token t of sequence b is row t % page_tokens of page
+                                  block_table[b][t / page_tokens] */
+  const int32_t* seq_lens;     /* [B] int32 keys per sequence, device memory; NULL: all T */
+} hga_kv_layout;
+
+/* hga_build_summaries over a ragged/paged cache (layout may be NULL = dense, all T). */
+int hga_build_summaries_ex(const void* K, int32_t dtype, const hga_kv_layout* layout,
+                           int64_t batch, int64_t kv_heads, int64_t seq_len, int64_t head_dim,
+                           int32_t chunk, int32_t group, float* chunk_mean, float* group_mean,
+                           void* stream);
+
+/* Recomputes, for every sequence, the summaries of the chunks holding its
+ * newest `newest` keys (1 <= newest <= seq_len) and of all their groups: the
+ * decode-step refresh after each sequence appended `newest` keys. */
+int hga_update_summaries_ex(const void* K, int32_t dtype, const hga_kv_layout* layout,
+                            int64_t batch, int64_t kv_heads, int64_t seq_len, int64_t head_dim,
+                            int32_t chunk, int32_t group, int64_t newest,
+                            float* chunk_mean, float* group_mean, void* stream);
+
+/* hga_route with per-sequence lengths (only layout->seq_lens is used; NULL
+ * layout = all T). Workspace as hga_route_workspace_size. */
+int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                 int32_t dtype, const float* chunk_mean, const float* group_mean, int32_t chunk,
+                 int32_t group, int32_t k_chunk, int32_t k_group, float scale,
+                 int32_t* chunk_idx, int32_t* group_idx,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* hga_attend over a ragged/paged cache (layout may be NULL = dense, all T).
+ * Paged K and V are page pools; group ids index the sequence's logical
+ * tokens. Workspace as hga_attend_workspace_size. */
+int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                  const void* K, const void* V, int32_t dtype, const int32_t* group_idx,
+                  int32_t k_group, int32_t group, float scale, void* O, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

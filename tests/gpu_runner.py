@@ -115,3 +115,20 @@ def check_sampled(w, inp, out, n_rows=256, seed=1, scale=None):
         f"group_exempt={st.group_exempt} O max-abs={err[0]:.3g} rel={err[1]:.3g} "
         f"({time.time() - t0:.1f}s)")
     return st, err
+
+
+def check_ragged(w, inp, seq_lens, out):
+    """Parity of a ragged batch: sequence b holds seq_lens[b] keys (a prefix of
+    the generated capacity-T cache) and its queries sit at seq_lens[b]-Nq+i. The
+    oracle runs on each sequence alone, on its own prefix."""
+    from synth.inputs import Inputs
+    results = []
+    for b, Tb in enumerate(seq_lens):
+        wb = w.with_(B=1, T=int(Tb))
+        sub = Inputs(wb, inp.seed, inp.Q[b:b + 1], inp.K[b:b + 1, :, :Tb], inp.V[b:b + 1, :, :Tb])
+        n_c, n_g = wb.n_chunks, wb.n_groups
+        ob = dict(cm=out["cm"][b:b + 1, :, :n_c], gm=out["gm"][b:b + 1, :, :n_g],
+                  cidx=out["cidx"][b:b + 1], gidx=out["gidx"][b:b + 1],
+                  O=out["O"][b:b + 1], lse=out["lse"][b:b + 1])
+        results.append(check_workload(wb, sub, ob))
+    return results

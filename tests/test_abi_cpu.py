@@ -125,3 +125,30 @@ def test_python_binding_rejects_cpu_tensors():
     K = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         hga.build_summaries(K, 16, 4)
+
+
+class _Lay(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+def test_paged_layout_rejected_before_launch():
+    L = ctypes.CDLL(hga.LIB_PATH)     # own handle: leave the binding's signatures alone
+    f = L.hga_build_summaries_ex
+    bad_kind = _Lay(7, 64, 128, 10, FAKE.value, None)
+    no_table = _Lay(1, 64, 128, 10, None, None)
+    page_not_group_multiple = _Lay(1, 48, 200, 10, FAKE.value, None)
+    too_few_pages = _Lay(1, 64, 10, 10, FAKE.value, None)
+    T = 8192
+    for lay, want in ((bad_kind, PARAM), (no_table, NULL), (page_not_group_multiple, PARAM),
+                      (too_few_pages, PARAM)):
+        got = f(FAKE, ctypes.c_int32(1), ctypes.byref(lay), ctypes.c_int64(4), ctypes.c_int64(2),
+                ctypes.c_int64(T), ctypes.c_int64(128), ctypes.c_int32(256), ctypes.c_int32(32),
+                FAKE, FAKE, None)
+        assert got == want, (lay.kind, got, want)
+    u = L.hga_update_summaries_ex
+    ok = _Lay(0, 0, 0, 0, None, None)
+    assert u(FAKE, ctypes.c_int32(1), ctypes.byref(ok), ctypes.c_int64(4), ctypes.c_int64(2),
+             ctypes.c_int64(T), ctypes.c_int64(128), ctypes.c_int32(256), ctypes.c_int32(32),
+             ctypes.c_int64(0), FAKE, FAKE, None) == PARAM          # newest < 1

@@ -233,3 +233,100 @@ def test_quality_proxy_matches_oracle():
     mass_ref = np.exp(lser_ref - lsed_ref)
     assert np.abs(mass_gpu - mass_ref).max() < 2e-3 * max(1.0, mass_ref.max())
     assert (mass_ref > 0).all() and (mass_ref <= 1 + 1e-9).all()   # a share of the dense mass
+
+
+def _ragged_case(Nq=1):
+    w = DECODE_64K.with_(name="ragged-b4-t8192", B=4, Hq=8, Hkv=2, T=8192, Nq=Nq, k_chunk=4,
+                         k_group=12, plants=2)
+    inp = generate(w)
+    seq_lens = [8192, 5000, 1234, 3001]
+    return w, inp, seq_lens
+
+
+def _run_ragged(w, inp, seq_lens, layout, K, V):
+    Q = to_dev(inp.Q, w.dtype)
+    cm, gm = hga.build_summaries_ex(K, w.chunk, w.group, layout=layout, seq_len=w.T)
+    cidx, gidx = hga.route_ex(Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group, layout=layout)
+    O, lse = hga.attend_ex(Q, K, V, gidx, w.group, layout=layout, seq_len=w.T)
+    torch.cuda.synchronize()
+    return dict(Q=Q, cm=cm, gm=gm, cidx=cidx, gidx=gidx, O=O, lse=lse)
+
+
+def _pages(w, inp, seq_lens, page_tokens, seed=5):
+    """The same caches cut into pages of page_tokens, scattered over a pool in a
+    random order; unused block-table entries are -1."""
+    rng = np.random.default_rng(seed)
+    need = [-(-int(t) // page_tokens) for t in seq_lens]
+    n_pages = sum(need) + 3
+    order = rng.permutation(n_pages)
+    max_pages = w.T // page_tokens
+    table = np.full((w.B, max_pages), -1, dtype=np.int32)
+    kp = np.zeros((n_pages, w.Hkv, page_tokens, w.D), dtype=np.float32)
+    vp = np.zeros_like(kp)
+    k = 0
+    for b in range(w.B):
+        for j in range(need[b]):
+            pid = int(order[k]); k += 1
+            table[b, j] = pid
+            kp[pid] = inp.K[b, :, j * page_tokens:(j + 1) * page_tokens]
+            vp[pid] = inp.V[b, :, j * page_tokens:(j + 1) * page_tokens]
+    return (to_dev(kp, w.dtype), to_dev(vp, w.dtype),
+            torch.from_numpy(table).cuda(), n_pages)
+
+
+@pytest.mark.parametrize("Nq", [1, 2])
+def test_ragged_dense_cache(Nq):
+    log(f"case ragged-dense Nq={Nq}")
+    w, inp, seq_lens = _ragged_case(Nq)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    layout = hga.Layout(seq_lens=lens)
+    out = _run_ragged(w, inp, seq_lens, layout, to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype))
+    from tests.gpu_runner import check_ragged
+    check_ragged(w, inp, seq_lens, out)
+
+
+def test_paged_cache_matches_ragged_dense():
+    log("case paged")
+    w, inp, seq_lens = _ragged_case(1)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    dense = _run_ragged(w, inp, seq_lens, hga.Layout(seq_lens=lens), to_dev(inp.K, w.dtype),
+                        to_dev(inp.V, w.dtype))
+    kp, vp, table, n_pages = _pages(w, inp, seq_lens, 64)
+    layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
+    paged = _run_ragged(w, inp, seq_lens, layout, kp, vp)
+    for b, Tb in enumerate(seq_lens):       # same arithmetic in the same order: bit-identical
+        nc, ng = -(-Tb // w.chunk), -(-Tb // w.group)
+        assert torch.equal(paged["cm"][b, :, :nc], dense["cm"][b, :, :nc])
+        assert torch.equal(paged["gm"][b, :, :ng], dense["gm"][b, :, :ng])
+    for k in ("cidx", "gidx", "O", "lse"):
+        assert torch.equal(paged[k], dense[k]), k
+    from tests.gpu_runner import check_ragged
+    check_ragged(w, inp, seq_lens, paged)
+    # decode refresh: every sequence's newest key changes; refresh = rebuild
+    for b, Tb in enumerate(seq_lens):
+        pid = int(table[b, (Tb - 1) // 64])
+        kp[pid, :, (Tb - 1) % 64] += 1.0
+    hga.update_summaries_ex(kp, w.chunk, w.group, 1, paged["cm"], paged["gm"], layout=layout,
+                            seq_len=w.T)
+    cm2, gm2 = hga.build_summaries_ex(kp, w.chunk, w.group, layout=layout, seq_len=w.T)
+    torch.cuda.synchronize()
+    for b, Tb in enumerate(seq_lens):
+        nc, ng = -(-Tb // w.chunk), -(-Tb // w.group)
+        assert torch.equal(paged["cm"][b, :, :nc], cm2[b, :, :nc])
+        assert torch.equal(paged["gm"][b, :, :ng], gm2[b, :, :ng])
+
+
+def test_ragged_query_before_first_key():
+    """A sequence shorter than Nq: the query at a negative position routes to
+    nothing (-1 ids, O = 0, lse = -inf); the next sees only token 0."""
+    log("case ragged-short")
+    w = DECODE_64K.with_(B=2, Hq=4, Hkv=1, T=512, Nq=2, k_chunk=1, k_group=2, plants=0)
+    inp = generate(w)
+    lens = torch.tensor([512, 1], dtype=torch.int32, device="cuda")
+    out = _run_ragged(w, inp, [512, 1], hga.Layout(seq_lens=lens), to_dev(inp.K, w.dtype),
+                      to_dev(inp.V, w.dtype))
+    assert (out["gidx"][1, :, 0] == -1).all() and (out["cidx"][1, :, 0] == -1).all()
+    assert (out["O"][1, :, 0] == 0).all() and torch.isinf(out["lse"][1, :, 0]).all()
+    assert (out["gidx"][1, :, 1, 0] == 0).all() and (out["gidx"][1, :, 1, 1:] == -1).all()
+    O1 = out["O"][1, :, 1].float().cpu().numpy()
+    assert np.abs(O1 - inp.V[1, 0, 0]).max() < 1e-2     # softmax over one token
