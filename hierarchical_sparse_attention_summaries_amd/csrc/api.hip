@@ -247,11 +247,15 @@ int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void
   a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
   a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
   a.seq_lens = layout ? layout->seq_lens : nullptr;
-  const hipError_t e =
-      (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
-                                         shape->n_queries, shape->head_dim))
-          ? hga::launch_route_prefill(a, as_stream(stream))
-          : hga::launch_route(a, dtype, plan, as_stream(stream));
+  hipError_t e;
+  if (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
+                                        shape->n_queries, shape->head_dim)) {
+    e = hga::launch_route_prefill(a, as_stream(stream));
+  } else if (hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries)) {
+    e = hga::launch_route_rows(a, dtype, as_stream(stream));
+  } else {
+    e = hga::launch_route(a, dtype, plan, as_stream(stream));
+  }
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 

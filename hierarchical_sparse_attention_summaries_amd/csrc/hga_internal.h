@@ -87,6 +87,11 @@ hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hi
 bool use_prefill_route(int dtype, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D);
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 
+// Few query rows (small decode batches): one workgroup per row runs both
+// levels on-chip (no workspace use, no cross-workgroup hand-off).
+bool use_row_route(int64_t B, int64_t Hq, int64_t Nq);
+hipError_t launch_route_rows(const RouteArgs& a, int dtype, hipStream_t stream);
+
 struct AttendPlan {
   int groups_per_wave;
   int n_splits;         // workgroups per query row

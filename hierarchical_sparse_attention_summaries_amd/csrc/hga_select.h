@@ -137,6 +137,8 @@ __device__ __forceinline__ int route_seq_len(const RouteArgs& a, int b) {
 }
 
 // Chunk ids one query keeps at most (the per-wave LDS list length).
-inline int kept_capacity(const RouteArgs& a) { return a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2; }
+__host__ __device__ inline int kept_capacity(const RouteArgs& a) {
+  return a.k_c + 2 > a.n_c ? a.n_c : a.k_c + 2;
+}
 
 }  // namespace hga
