@@ -25,7 +25,7 @@ constexpr int kMaxSplits = 32;  // workgroups per row at most (the plan guarante
 
 template <typename TKV, int D>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
-                                                          int n_splits) {
+                                                          int n_splits, int row_base) {
   constexpr int EPL = Elem<TKV>::kPer16;
   constexpr int LPR = D / EPL;        // lanes per token row
   constexpr int RPL = kWave / LPR;    // token rows per wave-wide load
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
   __shared__ bool s_last;
   __shared__ float s_part[kMaxSplits * (D + 2)];
 
-  const int row = blockIdx.x / n_splits;
+  const int row = row_base + static_cast<int>(blockIdx.x) / n_splits;
   const int split = blockIdx.x % n_splits;
   const int i = row % a.Nq;
   const int bh = row / a.Nq;
@@ -217,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
     store_shared(part, M);
     store_shared(part + 1, Lsum);
   }
-  if (!arrive_last(a.counters + row, static_cast<unsigned>(n_splits), &s_last)) return;
+  if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
+    return;
 
   // Pull every split's (m, l, o) into LDS with all loads in flight at once.
   const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
@@ -252,10 +253,18 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int grou
 template <typename TKV, int D>
 hipError_t launch_t(const AttendArgs& a, const AttendPlan& plan, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.Nq;
-  const unsigned blocks = static_cast<unsigned>(rows * plan.n_splits);
-  hipLaunchKernelGGL((attend_kernel<TKV, D>), dim3(blocks), dim3(kThreads), 0, stream, a,
-                     plan.groups_per_wave, plan.n_splits);
-  return hipGetLastError();
+  // With splits, slices of at most kMaxCounters rows (one counter each) that
+  // reuse the counters in stream order; without, one launch.
+  const int64_t slice = plan.n_splits > 1 ? kMaxCounters : rows;
+  for (int64_t base = 0; base < rows; base += slice) {
+    const int64_t n = rows - base < slice ? rows - base : slice;
+    hipLaunchKernelGGL((attend_kernel<TKV, D>), dim3(static_cast<unsigned>(n * plan.n_splits)),
+                       dim3(kThreads), 0, stream, a, plan.groups_per_wave, plan.n_splits,
+                       static_cast<int>(base));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -277,7 +286,7 @@ AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g) {
   const int waves_per_row = (k_g + gpw - 1) / gpw;
   pl.n_splits = (waves_per_row + kWaves - 1) / kWaves;
   pl.off_counters = 0;
-  pl.off_partials = align_up(static_cast<size_t>(rows) * sizeof(unsigned), 256);
+  pl.off_partials = kCounterBytes;
   const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;
   pl.bytes = align_up(pl.off_partials + part, 256);
   return pl;

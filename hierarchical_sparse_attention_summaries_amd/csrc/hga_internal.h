@@ -11,6 +11,12 @@ namespace hga {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
+// Every workspace starts with this many bytes of arrival counters. Nothing else
+// is ever stored there and every call leaves them at zero, so one workspace can
+// serve calls of any shape in turn. A launch uses at most kMaxCounters of them.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = static_cast<int>(kCounterBytes / sizeof(unsigned));
+
 // Largest number of items one wave selects from (middle chunks, or candidate
 // groups of the kept chunks), and of chunks one query keeps.
 constexpr int kMaxSelectItems = 4096;

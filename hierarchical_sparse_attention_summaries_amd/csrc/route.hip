@@ -33,7 +33,7 @@ constexpr int kMaxRows = 16;
 template <typename TQ, int D, int RM>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblocks,
                                                          int chunks_per_split, int n_splits,
-                                                         int e_sel, int kept_cap) {
+                                                         int e_sel, int kept_cap, int unit_base) {
   constexpr int DPL = 8;          // summary dims per lane (two 16-byte fp32 loads)
   constexpr int LPR = D / DPL;    // lanes per summary row
   constexpr int RPS = kWave / LPR;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
   float* s_stage = reinterpret_cast<float*>(s_dyn);
   __shared__ bool s_last;
 
-  const int unit = blockIdx.x / n_splits;
+  const int unit = unit_base + static_cast<int>(blockIdx.x) / n_splits;
   const int split = blockIdx.x % n_splits;
   const int qb = unit % n_qblocks;
   const int bkv = unit / n_qblocks;
@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
     }
   }
 
-  if (!arrive_last(a.counters + unit, static_cast<unsigned>(n_splits), &s_last)) return;
+  if (!arrive_last(a.counters + (unit - unit_base), static_cast<unsigned>(n_splits), &s_last))
+    return;
 
   int* s_kept = s_dyn + wave * kept_cap;
   for (int rho = wave; rho < rows_here; rho += kWaves) {
@@ -167,19 +168,28 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a, int n_qblo
 template <typename TQ, int D>
 hipError_t launch_rm(const RouteArgs& a, const RoutePlan& plan, int rm, int e_sel,
                      int kept_cap, hipStream_t stream) {
-  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv *
-                                                plan.n_qblocks * plan.n_splits);
+  const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * plan.n_qblocks;
   const size_t stage = static_cast<size_t>(rm) * plan.chunks_per_split * (1 + a.gpc) * sizeof(float);
   const size_t kept = static_cast<size_t>(kWaves) * kept_cap * sizeof(int);
   const size_t lds = stage > kept ? stage : kept;
-  if (rm == 8) {
-    hipLaunchKernelGGL((route_kernel<TQ, D, 8>), dim3(blocks), dim3(kThreads), lds, stream, a,
-                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap);
-  } else {
-    hipLaunchKernelGGL((route_kernel<TQ, D, 16>), dim3(blocks), dim3(kThreads), lds, stream, a,
-                       plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap);
+  // Slices of at most kMaxCounters units, one counter each; stream order lets
+  // a slice reuse the counters the previous one left at zero.
+  for (int64_t base = 0; base < units; base += kMaxCounters) {
+    const int64_t n = units - base < kMaxCounters ? units - base : kMaxCounters;
+    const dim3 grid(static_cast<unsigned>(n * plan.n_splits));
+    if (rm == 8) {
+      hipLaunchKernelGGL((route_kernel<TQ, D, 8>), grid, dim3(kThreads), lds, stream, a,
+                         plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap,
+                         static_cast<int>(base));
+    } else {
+      hipLaunchKernelGGL((route_kernel<TQ, D, 16>), grid, dim3(kThreads), lds, stream, a,
+                         plan.n_qblocks, plan.chunks_per_split, plan.n_splits, e_sel, kept_cap,
+                         static_cast<int>(base));
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -215,7 +225,7 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   pl.n_splits = static_cast<int>((n_c + pl.chunks_per_split - 1) / pl.chunks_per_split);
   const int64_t rows = B * Hq * Nq;
   pl.off_counters = 0;
-  pl.off_chunk_scores = align_up(static_cast<size_t>(units) * sizeof(unsigned), 256);
+  pl.off_chunk_scores = kCounterBytes;
   pl.off_group_scores = align_up(pl.off_chunk_scores + static_cast<size_t>(rows * n_c) * 4, 256);
   pl.bytes = align_up(pl.off_group_scores + static_cast<size_t>(rows * n_g) * 4, 256);
   pl.off_split = 0;

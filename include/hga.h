@@ -31,10 +31,11 @@
  *     launch failed; faults inside kernels surface at the caller's next
  *     synchronisation, as usual for HIP. Nothing throws, prints or aborts.
  *   - Inputs must be finite (no NaN/Inf in Q, K, V).
- *   - Workspaces: the first hga_*_workspace_size bytes must be zero-filled before
- *     their first use (e.g. allocate them zeroed). A call that returns HGA_OK leaves
- *     the workspace's counters at zero again, so a workspace can be reused
- *     call after call. Calls that may run concurrently must not share one.
+ *   - Workspaces: the first 64 KiB of a workspace hold arrival counters and must
+ *     be zero before the workspace's first use (e.g. allocate it zeroed). The
+ *     library stores nothing else there and every call leaves them at zero, so
+ *     one workspace (large enough for each call) can serve calls of any shape
+ *     in turn. Calls that may run concurrently must not share a workspace.
  */
 #ifndef HGA_H
 #define HGA_H

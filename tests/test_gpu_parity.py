@@ -75,6 +75,22 @@ PREFILL_SMALL = [
 ]
 
 
+# More than 1024 query rows without the MFMA path: the multi-workgroup route
+# (dense scoring of a KV head's summaries, last-arriving workgroup selects).
+FUSED_ROUTE = [
+    Workload("fused-f32-rows1600", 1, 8, 8, 128, 2048, 200, 64, 16, 5, 9, 1e4, "f32", 0),
+    Workload("fused-bf16-b40-decode", 40, 32, 4, 128, 4096, 1, 256, 32, 2, 4, 1e6, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("w", FUSED_ROUTE, ids=lambda w: w.name)
+def test_fused_route_many_rows(w):
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+
+
 @pytest.mark.parametrize("w", PREFILL_SMALL, ids=lambda w: w.name)
 def test_prefill_small(w):
     log(f"case {w.name}")
@@ -330,3 +346,21 @@ def test_ragged_query_before_first_key():
     assert (out["gidx"][1, :, 1, 0] == 0).all() and (out["gidx"][1, :, 1, 1:] == -1).all()
     O1 = out["O"][1, :, 1].float().cpu().numpy()
     assert np.abs(O1 - inp.V[1, 0, 0]).max() < 1e-2     # softmax over one token
+
+
+def test_one_workspace_serves_calls_of_different_shapes():
+    """Regression: a workspace reused across shapes. The first call's scores
+    must never land where the second call's arrival counters live."""
+    log("case workspace-reuse-across-shapes")
+    w1, w2 = FUSED_ROUTE
+    big = max(hga.route_workspace_bytes(hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D), w.chunk,
+                                        w.group, w.k_chunk, w.k_group) for w in (w1, w2))
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for w in (w1, w2, w1):
+        inp = generate(w)
+        Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+        cm, gm = hga.build_summaries(K, w.chunk, w.group)
+        cidx, gidx = hga.route(Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group, workspace=ws)
+        O, lse = hga.attend(Q, K, V, gidx, w.group)
+        torch.cuda.synchronize()
+        check_workload(w, inp, dict(cm=cm, gm=gm, cidx=cidx, gidx=gidx, O=O, lse=lse))
