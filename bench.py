@@ -2,9 +2,9 @@
 """HGA routed-attention decode benchmark on one MI355X.
 
 One step = one decode step of one attention layer over the whole batch, the
-full hot path: refresh the summaries of the chunk holding the newest key
-(hga_update_summaries), two-level routing (hga_route), exact attention over
-the routed tokens (hga_attend). Inputs are synthetic, seeded, already resident
+full hot path: refresh the summaries of the chunks holding the newest keys and
+route with them (hga_route_fresh_ex: steps 1-2, one launch for small batches),
+then exact attention over the routed tokens (hga_attend). Inputs are synthetic, seeded, already resident
 in HBM when timing starts. Caches are kept cold by rotating over enough copies
 of K/V/summaries that the routed working sets of one rotation exceed the
 256 MB Infinity Cache. Steps replay HIP graphs (one per copy) unless --no-graph.
@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["attend", "route", "update", "step", "copy"])
+    ap.add_argument("--only", choices=["attend", "route", "route_fresh", "update", "step", "copy"])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the batch-16 64K-context point of the context sweep")
     ap.add_argument("--no-host-tier", action="store_true",
@@ -205,17 +205,23 @@ def measure(w, args, primary: bool):
         hga.route(Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group, want_chunks=False,
                   group_idx=gidx, workspace=ws_r)
 
+    def k_route_fresh(s):
+        # steps 1-2 of a decode step: refresh the newest keys' summaries, route
+        K, V, cm, gm = sets[s]
+        hga.route_fresh_ex(Q, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                           want_chunks=False, group_idx=gidx, workspace=ws_r)
+
     def k_attend(s):
         K, V, cm, gm = sets[s]
         hga.attend(Q, K, V, gidx, w.group, out=O, lse=lse, workspace=ws_a)
 
     def step(s):
-        k_update(s)
-        k_route(s)
+        k_route_fresh(s)
         k_attend(s)
 
     if args.only:
-        fn = {"attend": k_attend, "route": k_route, "update": k_update, "step": step}[args.only]
+        fn = {"attend": k_attend, "route": k_route, "update": k_update, "step": step,
+              "route_fresh": k_route_fresh}[args.only]
         k_route(0)
         for k in range(args.warmup + args.steps):
             fn(k % S)
@@ -304,8 +310,8 @@ def measure(w, args, primary: bool):
     # launches of one kernel (rotating over the copies), the GPU kept busy
     # while the host enqueues; average = elapsed / n.
     n_k = max(50, min(args.steps, 400))
-    names = ("update", "route", "attend")
-    fns = (k_update, k_route, k_attend)
+    names = ("route_fresh", "attend", "update", "route")   # the step runs the first two
+    fns = (k_route_fresh, k_attend, k_update, k_route)
     kern_us = {}
     for nm, fn in zip(names, fns):
         reps = []
@@ -363,7 +369,7 @@ def measure(w, args, primary: bool):
                    "k_chunk": w.k_chunk, "k_group": w.k_group,
                    "routed_fraction": round(routed_tokens / (rows * w.T), 5),
                    "cold_cache_copies": S, "hip_graph": use_graph,
-                   "step": "update_summaries(newest Nq keys) + route + attend"},
+                   "step": "route_fresh_ex (newest-keys summary refresh + routing) + attend"},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,

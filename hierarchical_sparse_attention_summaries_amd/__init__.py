@@ -20,6 +20,7 @@ import torch
 __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summaries",
            "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
            "Layout", "build_summaries_ex", "update_summaries_ex", "route_ex", "attend_ex",
+           "route_fresh_ex",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
@@ -77,7 +78,7 @@ class Layout:
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libhga.so not built at {LIB_PATH}; run "
-                          "`python -m hierarchical_sparse_attention_summaries_amd.build`")
+                          "`python hierarchical_sparse_attention_summaries_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, f32, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                              ctypes.c_size_t)
@@ -103,6 +104,8 @@ def _load():
                                         f32, vp, vp, vp, sz, vp]),
         "hga_attend_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, i32, i32, f32,
                                          vp, vp, vp, sz, vp]),
+        "hga_route_fresh_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, i32, vp, vp, i32, i32,
+                                              i32, i32, f32, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -382,3 +385,26 @@ def attend_ex(Q, K, V, group_idx, group, layout=None, seq_len=None, scale=0.0, w
                               _ptr(out), _ptr(lse if want_lse else None), _ptr(ws), ws.numel(),
                               _stream(Q.device)), "hga_attend_ex")
     return out, (lse if want_lse else None)
+
+
+def route_fresh_ex(Q, K, chunk_mean, group_mean, seq_len, chunk, group, k_chunk, k_group,
+                   layout=None, scale=0.0, want_chunks=True, chunk_idx=None, group_idx=None,
+                   workspace=None):
+    """Decode step of steps 1-2: refresh the summaries of each sequence's newest
+    Nq keys from K, then route (one launch for small batches)."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    B, Hq, Nq, D = Q.shape
+    Hkv = chunk_mean.shape[1]
+    shape = _shape(Q, Hkv, seq_len)
+    nbytes = route_workspace_bytes(shape, chunk, group, k_chunk, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "route", nbytes)
+    if want_chunks and chunk_idx is None:
+        chunk_idx = torch.empty((B, Hq, Nq, k_chunk + 2), dtype=torch.int32, device=Q.device)
+    if group_idx is None:
+        group_idx = torch.empty((B, Hq, Nq, k_group), dtype=torch.int32, device=Q.device)
+    _check(_lib.hga_route_fresh_ex(ctypes.byref(shape), _lay(layout), _ptr(Q), _ptr(K),
+                                   _dtype_code(Q), _ptr(chunk_mean), _ptr(group_mean), chunk, group,
+                                   k_chunk, k_group, float(scale), _ptr(chunk_idx), _ptr(group_idx),
+                                   _ptr(ws), ws.numel(), _stream(Q.device)), "hga_route_fresh_ex")
+    return chunk_idx, group_idx

@@ -1,6 +1,8 @@
 """Builds libhga.so (gfx950 only) in this package directory with hipcc.
 
-    python -m hierarchical_sparse_attention_summaries_amd.build
+    python hierarchical_sparse_attention_summaries_amd/build.py
+
+(Run it as a script: importing the package loads the library it builds.)
 
 Every source under csrc/ is compiled to an object file in parallel, then
 linked into one shared library with a plain C ABI (include/hga.h).

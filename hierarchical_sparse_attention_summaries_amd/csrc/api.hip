@@ -203,11 +203,64 @@ int hga_route(const hga_shape* shape, const void* Q, int32_t dtype, const float*
                       k_group, scale, chunk_idx, group_idx, workspace, workspace_bytes, stream);
 }
 
+// Routing; with K_fresh, the row route also refreshes each sequence's newest
+// Nq keys' chunks from K_fresh (laid out as kv_fresh) before scoring.
+static int route_impl(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                      int32_t dtype, const float* chunk_mean, const float* group_mean,
+                      int32_t chunk, int32_t group, int32_t k_chunk, int32_t k_group, float scale,
+                      int32_t* chunk_idx, int32_t* group_idx, void* workspace,
+                      size_t workspace_bytes, void* stream, const void* K_fresh,
+                      const hga::KvLayout* kv_fresh);
+
 int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
                  int32_t dtype, const float* chunk_mean, const float* group_mean, int32_t chunk,
                  int32_t group, int32_t k_chunk, int32_t k_group, float scale,
                  int32_t* chunk_idx, int32_t* group_idx, void* workspace,
                  size_t workspace_bytes, void* stream) {
+  return route_impl(shape, layout, Q, dtype, chunk_mean, group_mean, chunk, group, k_chunk,
+                    k_group, scale, chunk_idx, group_idx, workspace, workspace_bytes, stream,
+                    nullptr, nullptr);
+}
+
+int hga_route_fresh_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                       const void* K, int32_t dtype, float* chunk_mean, float* group_mean,
+                       int32_t chunk, int32_t group, int32_t k_chunk, int32_t k_group,
+                       float scale, int32_t* chunk_idx, int32_t* group_idx, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K) return HGA_ERR_NULL;
+  if (!aligned16(K)) return HGA_ERR_LAYOUT;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  hga::KvLayout L;
+  st = to_layout(layout, shape->seq_len, group, &L);
+  if (st != HGA_OK) return st;
+  const bool fused = hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries) &&
+                     hga::row_route_can_refresh(shape->n_queries, chunk, group) &&
+                     !(dtype == HGA_BF16 &&
+                       hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
+                                              shape->n_queries, shape->head_dim));
+  if (!fused) {  // two launches: refresh, then route
+    st = summaries_common(K, dtype, layout, shape->batch, shape->kv_heads, shape->seq_len,
+                          shape->head_dim, chunk, group, 0, 0, shape->n_queries, chunk_mean,
+                          group_mean, stream);
+    if (st != HGA_OK) return st;
+    return route_impl(shape, layout, Q, dtype, chunk_mean, group_mean, chunk, group, k_chunk,
+                      k_group, scale, chunk_idx, group_idx, workspace, workspace_bytes, stream,
+                      nullptr, nullptr);
+  }
+  return route_impl(shape, layout, Q, dtype, chunk_mean, group_mean, chunk, group, k_chunk,
+                    k_group, scale, chunk_idx, group_idx, workspace, workspace_bytes, stream, K,
+                    &L);
+}
+
+static int route_impl(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                      int32_t dtype, const float* chunk_mean, const float* group_mean,
+                      int32_t chunk, int32_t group, int32_t k_chunk, int32_t k_group, float scale,
+                      int32_t* chunk_idx, int32_t* group_idx, void* workspace,
+                      size_t workspace_bytes, void* stream, const void* K_fresh,
+                      const hga::KvLayout* kv_fresh) {
   int st = check_shape(shape);
   if (st != HGA_OK) return st;
   if (layout && layout->kind != HGA_KV_DENSE && layout->kind != HGA_KV_PAGED) return HGA_ERR_PARAM;
@@ -247,11 +300,13 @@ int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void
   a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
   a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
   a.seq_lens = layout ? layout->seq_lens : nullptr;
+  a.K = K_fresh;
+  if (kv_fresh) a.kv = *kv_fresh;
   hipError_t e;
   if (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
                                         shape->n_queries, shape->head_dim)) {
     e = hga::launch_route_prefill(a, as_stream(stream));
-  } else if (hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries)) {
+  } else if (a.K || hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries)) {
     e = hga::launch_route_rows(a, dtype, as_stream(stream));
   } else {
     e = hga::launch_route(a, dtype, plan, as_stream(stream));

@@ -85,6 +85,11 @@ struct RouteArgs {
   unsigned* counters;  // workspace [B*Hkv*n_qblocks]
   uint16_t* split;     // workspace [B*Hkv, 2, n_c + n_g, D] bf16 (hi, lo); prefill path only
   const int32_t* seq_lens;  // [B] or null (all sequences hold T tokens)
+  // Decode-step refresh fused into routing: when K is set, the row route first
+  // recomputes the summaries of the chunks holding each sequence's newest Nq
+  // keys from K (through kv), writes them, and scores with them.
+  const void* K;
+  KvLayout kv;
 };
 hipError_t launch_route(const RouteArgs& a, int dtype, const RoutePlan& plan, hipStream_t stream);
 
@@ -97,6 +102,8 @@ hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 // levels on-chip (no workspace use, no cross-workgroup hand-off).
 bool use_row_route(int64_t B, int64_t Hq, int64_t Nq);
 hipError_t launch_route_rows(const RouteArgs& a, int dtype, hipStream_t stream);
+// Whether the row route can refresh the newest chunks itself (a.K set).
+bool row_route_can_refresh(int64_t Nq, int C, int G);
 
 struct AttendPlan {
   int groups_per_wave;

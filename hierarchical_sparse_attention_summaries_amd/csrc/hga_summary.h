@@ -1,0 +1,84 @@
+// Summaries of one chunk by one 8-wave workgroup (step 1 of HGA, abstract of
+// "Hierarchical Global Attention (HGA)", arXiv 2606.30709: the mean post-RoPE
+// key of each group and of the chunk). Shared by the summaries kernel and the
+// decode route that refreshes the newest chunk itself, so both produce the
+// same bits: the same rows go to the same lanes and are summed in the same
+// order.
+#pragma once
+
+#include "hga_device.h"
+#include "hga_internal.h"
+
+namespace hga {
+
+// Wave w sums groups g_first + w, g_first + w + WAVES, ... of chunk c of
+// (b, kv): 16-byte loads, UNROLL in flight per lane, fp32 accumulation, then a
+// fold over the rows of the group. put_group(g, col, sums, count) runs on the
+// lanes holding columns col .. col+EPL-1 of group g (sums not yet divided);
+// the waves' group sums meet in s_part, and after a workgroup barrier
+// put_chunk(d, chunk_sum, count) runs on threads d < D.
+template <typename TK, int D, int WAVES, typename PutGroup, typename PutChunk>
+__device__ __forceinline__ void chunk_summary(const TK* __restrict__ K, const KvLayout& L, int b,
+                                              int Hkv, int kv, int T, int Tb, int C, int G, int c,
+                                              float (*s_part)[D], PutGroup put_group,
+                                              PutChunk put_chunk) {
+  constexpr int EPL = Elem<TK>::kPer16;   // elements per lane per load
+  constexpr int LPR = D / EPL;            // lanes per key row
+  constexpr int RPL = kWave / LPR;        // rows per wave-wide load
+  constexpr int UNROLL = 8;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = (lane % LPR) * EPL;
+  const int sub = lane / LPR;
+  const int gpc = C / G;
+  const int g_first = c * gpc;
+  const int g_end = min(g_first + gpc, (Tb + G - 1) / G);
+
+  float csum[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) csum[e] = 0.f;
+  for (int g = g_first + wave; g < g_end; g += WAVES) {
+    const int t0 = g * G;
+    const int t1 = min(t0 + G, Tb);
+    const int64_t off = kv_offset(L, b, Hkv, kv, T, D, t0);  // the group's rows are consecutive
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    if (off >= 0) {
+      const TK* Kg = K + off;
+      for (int base = 0; base < t1 - t0; base += RPL * UNROLL) {
+        uint4 raw[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int t = base + u * RPL + sub;
+          raw[u] = t < t1 - t0 ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          float x[EPL];
+          widen(raw[u], x);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<LPR>(acc[e]);
+    if (sub == 0) put_group(g, col, acc, t1 - t0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) csum[e] += acc[e];
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_part[wave][col + e] = csum[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += s_part[w][threadIdx.x];
+    put_chunk(static_cast<int>(threadIdx.x), s, min(C, Tb - c * C));
+  }
+}
+
+}  // namespace hga

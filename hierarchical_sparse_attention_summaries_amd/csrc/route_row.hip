@@ -10,6 +10,7 @@
 #include "hga_device.h"
 #include "hga_internal.h"
 #include "hga_select.h"
+#include "hga_summary.h"
 
 namespace hga {
 namespace {
@@ -89,7 +90,10 @@ __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out
   return before;
 }
 
-template <typename TQ, int D, int E>
+constexpr int kFreshChunks = 2;   // chunks a refresh of <= C newest keys can touch
+constexpr int kFreshMaxGpc = 16;  // groups per chunk the refresh keeps in LDS
+
+template <typename TQ, int D, int E, bool FRESH>
 __global__ __launch_bounds__(kThreads) void route_row_kernel(RouteArgs a) {
   extern __shared__ float s_dyn[];
   // LDS: chunk scores [n_c] | candidate scores [cap * gpc] | kept chunks [cap] | chosen [max]
@@ -147,11 +151,51 @@ __global__ __launch_bounds__(kThreads) void route_row_kernel(RouteArgs a) {
       for (int e = 0; e < 8; ++e) q[e] *= a.scale;
     }
   }
-  const float* cm = a.chunk_mean + static_cast<size_t>(b * a.Hkv + kv) * a.n_c * D;
-  const float* gm = a.group_mean + static_cast<size_t>(b * a.Hkv + kv) * a.n_g * D;
+  const size_t bkv = static_cast<size_t>(b * a.Hkv + kv);
+  const float* cm = a.chunk_mean + bkv * a.n_c * D;
+  const float* gm = a.group_mean + bkv * a.n_g * D;
+
+  // Refresh: the chunks holding the sequence's newest Nq keys are recomputed
+  // from K (same bits as the summaries kernel), written out, and scored from
+  // LDS. Every row of this (sequence, KV head) writes the same values.
+  int cf = 1, cl = 0;  // refreshed chunk range (empty unless FRESH)
+  __shared__ float s_fc[FRESH ? kFreshChunks : 1][D];
+  __shared__ float s_fg[FRESH ? kFreshChunks * kFreshMaxGpc : 1][D];
+  __shared__ float s_part[FRESH ? kWaves : 1][D];
+  if constexpr (FRESH) {
+    constexpr int EPL = Elem<TQ>::kPer16;
+    const int Tb = route_seq_len(a, b);
+    cf = max(0, Tb - a.Nq) / a.C;
+    cl = (Tb - 1) / a.C;
+    float* cm_w = const_cast<float*>(cm);
+    float* gm_w = const_cast<float*>(gm);
+    for (int c = cf; c <= cl; ++c) {
+      chunk_summary<TQ, D, kWaves>(
+          static_cast<const TQ*>(a.K), a.kv, b, a.Hkv, kv, a.T, Tb, a.C, a.G, c, s_part,
+          [&](int g, int col, const float (&sum)[EPL], int count) {
+            const float inv = 1.f / static_cast<float>(count);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+              const float m = sum[e] * inv;
+              gm_w[static_cast<size_t>(g) * D + col + e] = m;
+              s_fg[g - cf * a.gpc][col + e] = m;
+            }
+          },
+          [&](int d, float sum, int count) {
+            const float m = sum / static_cast<float>(count);
+            cm_w[static_cast<size_t>(c) * D + d] = m;
+            s_fc[c - cf][d] = m;
+          });
+      __syncthreads();
+    }
+  }
+  auto chunk_row = [&](int c) -> const float* {
+    if (FRESH && c >= cf && c <= cl) return &s_fc[c - cf][0];
+    return cm + static_cast<size_t>(c) * D;
+  };
 
   // Level 1: chunks 0..L.
-  score_rows<D>(q, L + 1, [&](int c) { return cm + static_cast<size_t>(c) * D; }, s_cs);
+  score_rows<D>(q, L + 1, chunk_row, s_cs);
   __syncthreads();
   if (wave == 0) {
     int n_kept;
@@ -187,8 +231,9 @@ __global__ __launch_bounds__(kThreads) void route_row_kernel(RouteArgs a) {
     const int g = gid(t);
     return g < a.n_g && static_cast<int64_t>(g) * a.G <= p;
   };
-  score_rows<D>(q, n_cand, [&](int t) {
+  score_rows<D>(q, n_cand, [&](int t) -> const float* {
     const int g = gid(t);
+    if (FRESH && g / a.gpc >= cf && g / a.gpc <= cl) return &s_fg[g - cf * a.gpc][0];
     return gm + static_cast<size_t>(g < a.n_g ? g : 0) * D;
   }, s_gs);
   __syncthreads();
@@ -207,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void route_row_kernel(RouteArgs a) {
   }
 }
 
-template <typename TQ, int D>
+template <typename TQ, int D, bool FRESH>
 hipError_t launch_td(const RouteArgs& a, int e_sel, size_t lds, hipStream_t stream) {
   const int64_t units = static_cast<int64_t>(a.B) * a.Hkv;
   const int64_t rpu = static_cast<int64_t>(a.Hq / a.Hkv) * a.Nq;
@@ -215,7 +260,7 @@ hipError_t launch_td(const RouteArgs& a, int e_sel, size_t lds, hipStream_t stre
   switch (e_sel) {
 #define HGA_ROW_CASE(EV)                                                                         \
   case EV:                                                                                       \
-    hipLaunchKernelGGL((route_row_kernel<TQ, D, EV>), grid, dim3(kThreads), lds, stream, a);     \
+    hipLaunchKernelGGL((route_row_kernel<TQ, D, EV, FRESH>), grid, dim3(kThreads), lds, stream, a); \
     break;
     HGA_ROW_CASE(1)
     HGA_ROW_CASE(2)
@@ -227,7 +272,7 @@ hipError_t launch_td(const RouteArgs& a, int e_sel, size_t lds, hipStream_t stre
     HGA_ROW_CASE(16)
     HGA_ROW_CASE(32)
     default:
-      hipLaunchKernelGGL((route_row_kernel<TQ, D, 64>), grid, dim3(kThreads), lds, stream, a);
+      hipLaunchKernelGGL((route_row_kernel<TQ, D, 64, FRESH>), grid, dim3(kThreads), lds, stream, a);
       break;
 #undef HGA_ROW_CASE
   }
@@ -238,16 +283,27 @@ hipError_t launch_td(const RouteArgs& a, int e_sel, size_t lds, hipStream_t stre
 
 bool use_row_route(int64_t B, int64_t Hq, int64_t Nq) { return B * Hq * Nq <= 1024; }
 
+bool row_route_can_refresh(int64_t Nq, int C, int G) {
+  return Nq <= C && C / G <= kFreshMaxGpc;
+}
+
 hipError_t launch_route_rows(const RouteArgs& a, int dtype, hipStream_t stream) {
   const int cap = kept_capacity(a);
   const size_t lds = (static_cast<size_t>(a.n_c) + static_cast<size_t>(cap) * a.gpc) * 4 +
                      static_cast<size_t>(cap) * 4 + static_cast<size_t>(kMaxSelectItems) * 4;
   const int e_sel = select_regs(a);
+  if (a.K) {
+    if (dtype == kF32)
+      return a.D == 64 ? launch_td<float, 64, true>(a, e_sel, lds, stream)
+                       : launch_td<float, 128, true>(a, e_sel, lds, stream);
+    return a.D == 64 ? launch_td<uint16_t, 64, true>(a, e_sel, lds, stream)
+                     : launch_td<uint16_t, 128, true>(a, e_sel, lds, stream);
+  }
   if (dtype == kF32)
-    return a.D == 64 ? launch_td<float, 64>(a, e_sel, lds, stream)
-                     : launch_td<float, 128>(a, e_sel, lds, stream);
-  return a.D == 64 ? launch_td<uint16_t, 64>(a, e_sel, lds, stream)
-                   : launch_td<uint16_t, 128>(a, e_sel, lds, stream);
+    return a.D == 64 ? launch_td<float, 64, false>(a, e_sel, lds, stream)
+                     : launch_td<float, 128, false>(a, e_sel, lds, stream);
+  return a.D == 64 ? launch_td<uint16_t, 64, false>(a, e_sel, lds, stream)
+                   : launch_td<uint16_t, 128, false>(a, e_sel, lds, stream);
 }
 
 }  // namespace hga

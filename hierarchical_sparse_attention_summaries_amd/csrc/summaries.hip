@@ -13,6 +13,7 @@
 // meet in LDS. HBM-bound: every key is read exactly once.
 #include "hga_device.h"
 #include "hga_internal.h"
+#include "hga_summary.h"
 
 namespace hga {
 namespace {
@@ -25,11 +26,7 @@ __global__ __launch_bounds__(kThreads) void summaries_kernel(
     const TK* __restrict__ K, KvLayout L, float* __restrict__ chunk_mean,
     float* __restrict__ group_mean, int Hkv, int T, int C, int G, int n_c, int n_g, int c_begin,
     int n_chunks_here, int newest) {
-  constexpr int EPL = Elem<TK>::kPer16;   // elements per lane per load
-  constexpr int LPR = D / EPL;            // lanes per key row
-  constexpr int RPL = kWave / LPR;        // rows per wave-wide load
-  constexpr int UNROLL = 8;               // loads in flight per lane
-
+  constexpr int EPL = Elem<TK>::kPer16;
   __shared__ float s_part[kWaves][D];
 
   const int bh = blockIdx.x / n_chunks_here;
@@ -39,69 +36,17 @@ __global__ __launch_bounds__(kThreads) void summaries_kernel(
   const int c0 = newest > 0 ? max(0, Tb - newest) / C : c_begin;
   const int c = c0 + blockIdx.x % n_chunks_here;
   if (c * C >= Tb) return;  // beyond this sequence's keys: nothing to summarise
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int col = (lane % LPR) * EPL;
-  const int sub = lane / LPR;             // row slot within a load
-
-  const int gpc = C / G;
-  const int g_first = c * gpc;
-  const int g_end = min(g_first + gpc, (Tb + G - 1) / G);
-
-  float csum[EPL];
+  chunk_summary<TK, D, kWaves>(
+      K, L, b, Hkv, kv, T, Tb, C, G, c, s_part,
+      [&](int g, int col, const float (&sum)[EPL], int count) {
+        const float inv = 1.f / static_cast<float>(count);
+        float* dst = group_mean + (static_cast<size_t>(bh) * n_g + g) * D + col;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) csum[e] = 0.f;
-
-  for (int g = g_first + wave; g < g_end; g += kWaves) {
-    const int t0 = g * G;
-    const int t1 = min(t0 + G, Tb);
-    const int64_t off = kv_offset(L, b, Hkv, kv, T, D, t0);  // the group's rows are consecutive
-    float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    if (off >= 0) {
-      const TK* Kg = K + off;
-      for (int base = 0; base < t1 - t0; base += RPL * UNROLL) {
-        uint4 raw[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int t = base + u * RPL + sub;
-          raw[u] = t < t1 - t0 ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          float x[EPL];
-          widen(raw[u], x);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] += x[e];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<LPR>(acc[e]);
-    const float inv = 1.f / static_cast<float>(t1 - t0);
-    if (sub == 0) {
-      float* dst = group_mean + (static_cast<size_t>(bh) * n_g + g) * D + col;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) csum[e] += acc[e];
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) s_part[wave][col + e] = csum[e];
-  }
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += s_part[w][threadIdx.x];
-    const int t0 = c * C;
-    const int t1 = min(t0 + C, Tb);
-    chunk_mean[(static_cast<size_t>(bh) * n_c + c) * D + threadIdx.x] =
-        s / static_cast<float>(t1 - t0);
-  }
+        for (int e = 0; e < EPL; ++e) dst[e] = sum[e] * inv;
+      },
+      [&](int d, float sum, int count) {
+        chunk_mean[(static_cast<size_t>(bh) * n_c + c) * D + d] = sum / static_cast<float>(count);
+      });
 }
 
 template <typename TK, int D>

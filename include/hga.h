@@ -217,6 +217,19 @@ int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void
                  int32_t* chunk_idx, int32_t* group_idx,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode-step form of step 1 + step 2: hga_update_summaries_ex(newest = Nq)
+ * followed by hga_route_ex, with the same results bit for bit. For small
+ * batches (B*Hq*Nq <= 1024, Nq <= chunk, chunk/group <= 16, not the MFMA
+ * prefill case) it runs as one launch: each routing workgroup recomputes the
+ * newest chunks of its sequence from K, writes them to chunk_mean/group_mean
+ * and scores with them; otherwise it enqueues the two calls. K is the cache the
+ * layout describes. Workspace as hga_route_workspace_size. */
+int hga_route_fresh_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                       const void* K, int32_t dtype, float* chunk_mean, float* group_mean,
+                       int32_t chunk, int32_t group, int32_t k_chunk, int32_t k_group,
+                       float scale, int32_t* chunk_idx, int32_t* group_idx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* hga_attend over a ragged/paged cache (layout may be NULL = dense, all T).
  * Paged K and V are page pools; group ids index the sequence's logical
  * tokens. Workspace as hga_attend_workspace_size. */
