@@ -2,18 +2,19 @@
 """HGA routed-attention decode benchmark on one MI355X.
 
 One step = one decode step of one attention layer over the whole batch, the
-full hot path: refresh the summaries of the chunks holding the newest keys and
-route with them (hga_route_fresh_ex: steps 1-2, one launch for small batches),
-then exact attention over the routed tokens (hga_attend). Inputs are synthetic, seeded, already resident
-in HBM when timing starts. Caches are kept cold by rotating over enough copies
+full hot path in one call (hga_decode_step_ex): refresh the summaries of the
+chunks holding the newest keys, route with them, and attend exactly over the
+routed tokens (one launch for small batches). Inputs are synthetic, seeded,
+already resident in HBM when timing starts. Caches are kept cold by rotating over enough copies
 of K/V/summaries that the routed working sets of one rotation exceed the
 256 MB Infinity Cache. Steps replay HIP graphs (one per copy) unless --no-graph.
 
 Prints one JSON line (metric, value in decode tokens/s, roofline of the
-attention kernel, CPU-oracle baseline, per-kernel times, latency percentiles).
+attention kernel and of the whole step, CPU-oracle baseline, per-kernel times,
+latency percentiles).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
-    python bench.py --only attend|route|update|copy   # short runs for rocprofv3
+    python bench.py --only decode|attend|route|route_fresh|update|copy   # short runs for rocprofv3
 """
 from __future__ import annotations
 
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["attend", "route", "route_fresh", "update", "step", "copy"])
+    ap.add_argument("--only", choices=["decode", "attend", "route", "route_fresh", "update", "step",
+                                       "copy"])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the batch-16 64K-context point of the context sweep")
     ap.add_argument("--no-host-tier", action="store_true",
@@ -62,20 +64,26 @@ def kernel_source_hash(names):
     return h.hexdigest()[:16]
 
 
-ATTEND_SOURCES = ["attend.hip", "hga_device.h", "hga_internal.h"]
+# Sources each profiled kernel is built from: a stored counter reading is used
+# only while they hash as they did when it was taken.
+KERNEL_SOURCES = {
+    "attend": ["attend.hip", "hga_attend_body.h", "hga_device.h", "hga_internal.h"],
+    "decode_step": ["decode.hip", "hga_attend_body.h", "hga_route_row_body.h", "hga_device.h",
+                    "hga_internal.h", "hga_select.h", "hga_summary.h"],
+}
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"hga_attend_{workload}_counters.md")
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"hga_{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None, None
     m = re.search(r"^traffic_json: (\{.*\})\s*$", open(path).read(), flags=re.M)
     if not m:
         return None, None
     d = json.loads(m.group(1))
-    if d.get("src_hash") != kernel_source_hash(ATTEND_SOURCES):
+    if d.get("src_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
         return None, d
     fetch = d["fetch_kib"] * 1024 * d["fetch_scale"]
     write = d["write_kib"] * 1024 * d["write_scale"]
@@ -125,7 +133,8 @@ def main():
             sec = measure(w2, sec_args, primary=False)
             out["secondary"] = {k: sec[k] for k in ("config", "value", "unit", "ms_per_step",
                                                     "steps", "hbm_gbs_step", "roofline",
-                                                    "kernels_us", "latency_us")}
+                                                    "roofline_step", "kernels_us",
+                                                    "latency_us")}
     print(json.dumps(out))
 
 
@@ -151,28 +160,53 @@ def measure(w, args, primary: bool):
         K0 = torch.from_numpy(inp.K).to(dev, tdt)
         V0 = torch.from_numpy(inp.V).to(dev, tdt)
     cm0, gm0 = hga.build_summaries(K0, w.chunk, w.group)
-    _, gidx0 = hga.route(Q, cm0, gm0, w.T, w.chunk, w.group, w.k_chunk, w.k_group, want_chunks=False)
+    cidx0, gidx0 = hga.route(Q, cm0, gm0, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
     torch.cuda.synchronize()
 
-    # Algorithmic bytes of one step (what the method must move).
+    # Algorithmic bytes (what the method must move).
+    # The attention kernel alone: every row's routed K/V tokens, Q, O, lse, ids.
     g = gidx0.cpu().numpy()
-    routed_tokens = 0
-    for b in range(w.B):
-        for h in range(w.Hq):
-            for i in range(w.Nq):
-                p = w.T - w.Nq + i
-                for gg in g[b, h, i]:
-                    if gg >= 0:
-                        routed_tokens += int(max(0, min(gg * w.group + w.group, p + 1) - gg * w.group))
+    c = cidx0.cpu().numpy()
+    r = w.Hq // w.Hkv
     rows = w.B * w.Hq * w.Nq
-    n_c, n_g = w.n_chunks, w.n_groups
+    gpc = w.chunk // w.group
+
+    def tokens_of(gg, p):
+        return max(0, min(gg * w.group + w.group, p + 1) - gg * w.group)
+
+    routed_tokens = 0
+    union_tokens = 0      # K/V tokens routed to any query of a (sequence, KV head)
+    union_cand = 0        # candidate group summaries read by any query of a (sequence, KV head)
+    for b in range(w.B):
+        for kv in range(w.Hkv):
+            seen = {}
+            cands = set()
+            for h in range(kv * r, (kv + 1) * r):
+                for i in range(w.Nq):
+                    p = w.T - w.Nq + i
+                    for gg in g[b, h, i]:
+                        if gg >= 0:
+                            n = tokens_of(int(gg), p)
+                            routed_tokens += n
+                            seen[int(gg)] = max(seen.get(int(gg), 0), n)
+                    for cc in c[b, h, i]:
+                        if cc >= 0:
+                            cands.update(int(cc) * gpc + j for j in range(gpc)
+                                         if int(cc) * gpc + j < w.n_groups)
+            union_tokens += sum(seen.values())
+            union_cand += len(cands)
     attend_bytes = routed_tokens * w.D * 2 * esize + rows * (2 * w.D * esize + 4 * w.k_group + 4)
-    route_bytes = w.B * w.Hkv * (n_c + n_g) * w.D * 4 + rows * w.D * esize + rows * 4 * w.k_group
-    c_first = (w.T - w.Nq) // w.chunk              # chunks holding the newest Nq keys
+    # One decode step: Q, all chunk summaries, the candidate groups' summaries,
+    # the routed K/V (union per KV head), O, lse and ids, plus the refresh of the
+    # chunks holding the newest keys (their keys read, their summaries written).
+    c_first = (w.T - w.Nq) // w.chunk
     n_upd = w.n_chunks - c_first
     upd_tokens = w.T - c_first * w.chunk
-    update_bytes = w.B * w.Hkv * (upd_tokens * w.D * esize + n_upd * (1 + w.chunk // w.group) * w.D * 4)
-    step_bytes = attend_bytes + route_bytes + update_bytes
+    update_bytes = w.B * w.Hkv * (upd_tokens * w.D * esize + n_upd * (1 + gpc) * w.D * 4)
+    step_bytes = (rows * w.D * esize + w.B * w.Hkv * w.n_chunks * w.D * 4 + union_cand * w.D * 4
+                  + union_tokens * w.D * 2 * esize + rows * (w.D * esize + 4 + 4 * w.k_group)
+                  + update_bytes)
+    route_bytes = step_bytes - attend_bytes
 
     # Cold-cache rotation: copies at distinct addresses so that one rotation's
     # routed working sets exceed the Infinity Cache.
@@ -192,6 +226,8 @@ def measure(w, args, primary: bool):
                        dtype=torch.uint8, device=dev)
     ws_a = torch.zeros(hga.attend_workspace_bytes(shape, w.group, w.k_group), dtype=torch.uint8,
                        device=dev)
+    ws_d = torch.zeros(hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk,
+                                                       w.k_group), dtype=torch.uint8, device=dev)
     gidx = torch.empty_like(gidx0)
     O = torch.empty_like(Q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
@@ -215,13 +251,19 @@ def measure(w, args, primary: bool):
         K, V, cm, gm = sets[s]
         hga.attend(Q, K, V, gidx, w.group, out=O, lse=lse, workspace=ws_a)
 
-    def step(s):
-        k_route_fresh(s)
-        k_attend(s)
+    def k_decode(s):
+        # the whole decode step: refresh, route, attend
+        K, V, cm, gm = sets[s]
+        hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                           want_chunks=False, group_idx=gidx, out=O, lse=lse, workspace=ws_d)
+
+    step = k_decode
+    decode_one_launch = hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk,
+                                                   w.k_group)
 
     if args.only:
         fn = {"attend": k_attend, "route": k_route, "update": k_update, "step": step,
-              "route_fresh": k_route_fresh}[args.only]
+              "route_fresh": k_route_fresh, "decode": k_decode}[args.only]
         k_route(0)
         for k in range(args.warmup + args.steps):
             fn(k % S)
@@ -231,9 +273,14 @@ def measure(w, args, primary: bool):
         sys.exit(0)
 
     # correctness guard: the timed path reproduces the reference run's routing
+    # and the standalone attention's output
     step(0)
     torch.cuda.synchronize()
     assert torch.equal(gidx, gidx0), "routing changed between runs"
+    O_step = O.clone()
+    k_attend(0)
+    torch.cuda.synchronize()
+    assert float((O_step.float() - O.float()).abs().max()) <= 2e-2, "decode step != attend"
 
     use_graph = not args.no_graph
     singles, chain = [], None
@@ -310,8 +357,8 @@ def measure(w, args, primary: bool):
     # launches of one kernel (rotating over the copies), the GPU kept busy
     # while the host enqueues; average = elapsed / n.
     n_k = max(50, min(args.steps, 400))
-    names = ("route_fresh", "attend", "update", "route")   # the step runs the first two
-    fns = (k_route_fresh, k_attend, k_update, k_route)
+    names = ("decode_step", "route_fresh", "attend", "update", "route")   # the step is the first
+    fns = (k_decode, k_route_fresh, k_attend, k_update, k_route)
     kern_us = {}
     for nm, fn in zip(names, fns):
         reps = []
@@ -326,7 +373,7 @@ def measure(w, args, primary: bool):
             reps.append(e0.elapsed_time(e1) * 1e3 / n_k)
         kern_us[nm] = {"avg": statistics.median(reps), "launches": 3 * n_k}
     attend_us = kern_us["attend"]["avg"]
-    achieved = attend_bytes / (attend_us * 1e-6) / 1e9
+    decode_us = kern_us["decode_step"]["avg"]
 
     quality = None
     if primary and not w.host_kv and w.Nq == 1:
@@ -334,16 +381,24 @@ def measure(w, args, primary: bool):
     host = None
     if w.host_kv:
         kv_bytes = 2 * K0.numel() * esize
-        hbm = sum(t.numel() * t.element_size() for t in (Q, cm0, gm0, O, lse, gidx0, ws_r, ws_a))
+        hbm = sum(t.numel() * t.element_size() for t in (Q, cm0, gm0, O, lse, gidx0, ws_d))
         host = {"kv_bytes_in_host_memory": kv_bytes, "hbm_bytes_resident": hbm,
                 "fetched_bytes_per_token": attend_bytes // (w.B * w.Nq),
                 "host_link_gbs": round(attend_bytes / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
 
-    traffic, tinfo = stored_traffic(w.name)
-    roofline = {"kernel": "hga_attend", "bound": "hbm", "achieved": round(achieved, 1),
+    def roof(kernel, nbytes, us):
+        traffic, _ = stored_traffic(kernel, w.name)
+        achieved = nbytes / (us * 1e-6) / 1e9
+        return {"kernel": f"hga_{kernel}", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "alg_bytes_per_launch": attend_bytes,
-                "avg_launch_us": round(attend_us, 3)}
+                "traffic": traffic, "alg_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
+
+    # The dominant kernel: attention moves the routed K/V, almost all of a
+    # step's bytes. Beside it, the whole step (one launch for small batches)
+    # against the step's algorithmic bytes.
+    roofline = roof("attend", attend_bytes, attend_us)
+    roofline_step = roof("decode_step", step_bytes, decode_us)
+    roofline_step["launches"] = 1 if decode_one_launch else 2
 
     # ---------------- CPU oracle baseline (host cores, bounded sample)
     cpu = None
@@ -369,10 +424,11 @@ def measure(w, args, primary: bool):
                    "k_chunk": w.k_chunk, "k_group": w.k_group,
                    "routed_fraction": round(routed_tokens / (rows * w.T), 5),
                    "cold_cache_copies": S, "hip_graph": use_graph,
-                   "step": "route_fresh_ex (newest-keys summary refresh + routing) + attend"},
+                   "step": "decode_step_ex (newest-keys summary refresh + routing + attention)"},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,
+        "roofline_step": roofline_step,
         "kernels_us": {k: round(v["avg"], 3) for k, v in kern_us.items()},
         "latency_us": {"p50": round(pct(lat, 0.5), 2), "p95": round(pct(lat, 0.95), 2),
                        "p99": round(pct(lat, 0.99), 2)},

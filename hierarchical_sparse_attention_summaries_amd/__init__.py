@@ -106,6 +106,10 @@ def _load():
                                          vp, vp, vp, sz, vp]),
         "hga_route_fresh_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, i32, vp, vp, i32, i32,
                                               i32, i32, f32, vp, vp, vp, sz, vp]),
+        "hga_decode_step_workspace_size": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, P(sz)]),
+        "hga_decode_step_one_launch": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, i32, P(i32)]),
+        "hga_decode_step_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, vp, i32,
+                                              i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -408,3 +412,54 @@ def route_fresh_ex(Q, K, chunk_mean, group_mean, seq_len, chunk, group, k_chunk,
                                    k_chunk, k_group, float(scale), _ptr(chunk_idx), _ptr(group_idx),
                                    _ptr(ws), ws.numel(), _stream(Q.device)), "hga_route_fresh_ex")
     return chunk_idx, group_idx
+
+
+def decode_step_workspace_bytes(shape: Shape, chunk, group, k_chunk, k_group) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.hga_decode_step_workspace_size(ctypes.byref(shape), chunk, group, k_chunk,
+                                               k_group, ctypes.byref(n)),
+           "hga_decode_step_workspace_size")
+    return n.value
+
+
+def decode_step_one_launch(shape: Shape, dtype: str, chunk, group, k_chunk, k_group) -> bool:
+    """Whether decode_step_ex runs these arguments as a single kernel launch."""
+    one = ctypes.c_int32()
+    code = {"f32": F32, "bf16": BF16}[dtype]
+    _check(_lib.hga_decode_step_one_launch(ctypes.byref(shape), code, chunk, group, k_chunk,
+                                           k_group, ctypes.byref(one)),
+           "hga_decode_step_one_launch")
+    return bool(one.value)
+
+
+def decode_step_ex(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chunk, k_group,
+                   layout=None, scale=0.0, want_chunks=True, want_lse=True, chunk_idx=None,
+                   group_idx=None, out=None, lse=None, workspace=None):
+    """One decode step: refresh the summaries of each sequence's newest Nq keys
+    from K, route, and attend (one launch for small batches). Returns
+    (O, lse, chunk_idx, group_idx)."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    _need(V, "V", 4, host_ok=True)
+    B, Hq, Nq, D = Q.shape
+    Hkv = chunk_mean.shape[1]
+    if tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K and V differ in shape")
+    shape = _shape(Q, Hkv, seq_len)
+    nbytes = decode_step_workspace_bytes(shape, chunk, group, k_chunk, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "decode", nbytes)
+    if want_chunks and chunk_idx is None:
+        chunk_idx = torch.empty((B, Hq, Nq, k_chunk + 2), dtype=torch.int32, device=Q.device)
+    if group_idx is None:
+        group_idx = torch.empty((B, Hq, Nq, k_group), dtype=torch.int32, device=Q.device)
+    if out is None:
+        out = torch.empty_like(Q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    _check(_lib.hga_decode_step_ex(ctypes.byref(shape), _lay(layout), _ptr(Q), _ptr(K), _ptr(V),
+                                   _dtype_code(Q), _ptr(chunk_mean), _ptr(group_mean), chunk,
+                                   group, k_chunk, k_group, float(scale),
+                                   _ptr(chunk_idx if want_chunks else None), _ptr(group_idx),
+                                   _ptr(out), _ptr(lse if want_lse else None), _ptr(ws),
+                                   ws.numel(), _stream(Q.device)), "hga_decode_step_ex")
+    return out, (lse if want_lse else None), chunk_idx, group_idx

@@ -66,6 +66,102 @@ int check_route_params(const hga_shape* s, int32_t chunk, int32_t group, int32_t
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+float default_scale(float scale, int64_t D) {
+  return scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(D));
+}
+
+hga::RouteArgs route_args(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                          const float* chunk_mean, const float* group_mean, int32_t chunk,
+                          int32_t group, int32_t k_chunk, int32_t k_group, float scale,
+                          int32_t* chunk_idx, int32_t* group_idx, void* workspace,
+                          const hga::RoutePlan& plan) {
+  hga::RouteArgs a{};
+  a.Q = Q;
+  a.chunk_mean = chunk_mean;
+  a.group_mean = group_mean;
+  a.B = static_cast<int>(shape->batch);
+  a.Hq = static_cast<int>(shape->q_heads);
+  a.Hkv = static_cast<int>(shape->kv_heads);
+  a.Nq = static_cast<int>(shape->n_queries);
+  a.T = static_cast<int>(shape->seq_len);
+  a.D = static_cast<int>(shape->head_dim);
+  a.C = chunk;
+  a.G = group;
+  a.gpc = chunk / group;
+  a.n_c = static_cast<int>((shape->seq_len + chunk - 1) / chunk);
+  a.n_g = static_cast<int>((shape->seq_len + group - 1) / group);
+  a.k_c = k_chunk;
+  a.k_g = k_group;
+  a.scale = default_scale(scale, shape->head_dim);
+  a.chunk_idx = chunk_idx;
+  a.group_idx = group_idx;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
+  a.chunk_scores = reinterpret_cast<float*>(ws + plan.off_chunk_scores);
+  a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
+  a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
+  a.seq_lens = layout ? layout->seq_lens : nullptr;
+  return a;
+}
+
+hga::AttendArgs attend_args(const hga_shape* shape, const hga::KvLayout& L, const void* Q,
+                            const void* K, const void* V, const int32_t* group_idx,
+                            int32_t k_group, int32_t group, float scale, void* O, float* lse,
+                            void* workspace, const hga::AttendPlan& plan) {
+  hga::AttendArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.group_idx = group_idx;
+  a.O = O;
+  a.lse = lse;
+  a.B = static_cast<int>(shape->batch);
+  a.Hq = static_cast<int>(shape->q_heads);
+  a.Hkv = static_cast<int>(shape->kv_heads);
+  a.Nq = static_cast<int>(shape->n_queries);
+  a.T = static_cast<int>(shape->seq_len);
+  a.D = static_cast<int>(shape->head_dim);
+  a.G = group;
+  a.k_g = k_group;
+  a.scale = default_scale(scale, shape->head_dim);
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
+  a.partials = reinterpret_cast<float*>(ws + plan.off_partials);
+  a.kv = L;
+  return a;
+}
+
+// Whether hga_route_fresh_ex refreshes inside the row route (one launch), and
+// hga_decode_step_ex runs as one launch.
+// `decode`: inside the one-launch decode step (attention's LDS beside it).
+bool row_fresh_fused(const hga_shape* s, int32_t dtype, int32_t chunk, int32_t group,
+                     int32_t k_chunk, int32_t k_group, bool decode) {
+  if (decode && !hga::decode_step_one_launch(s->batch, s->q_heads, s->kv_heads, s->n_queries,
+                                             s->head_dim, group, k_group))
+    return false;
+  return hga::use_row_route(s->batch, s->q_heads, s->n_queries, s->seq_len, s->head_dim, chunk,
+                            group, k_chunk, k_group, true,
+                            decode ? hga::decode_step_lds(s->head_dim) : 0) &&
+         !(dtype == HGA_BF16 &&
+           hga::use_prefill_route(dtype, s->q_heads, s->kv_heads, s->n_queries, s->head_dim));
+}
+
+// Workspace of hga_decode_step_ex. The two-call form runs routing and then
+// attention in stream order over the same workspace; the one-launch form keeps
+// its ready flags at counter words [0, rows) and the attention's arrival
+// counters at words [kDecodeAttendCounters, +rows) (rows <= 1024 there), and
+// the attention partials after the counters, as every plan does.
+constexpr int kDecodeAttendCounters = 8192;
+size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
+                              int32_t k_group) {
+  const int64_t rows = s->batch * s->q_heads * s->n_queries;
+  return std::max({hga::plan_route(s->batch, s->q_heads, s->kv_heads, s->n_queries, s->seq_len,
+                                   chunk, group, k_chunk, k_group)
+                       .bytes,
+                   hga::plan_attend(rows, s->head_dim, group, k_group).bytes,
+                   hga::plan_attend(rows, s->head_dim, group, k_group, 8).bytes});
+}
+
 // Checks a caller's K/V layout against the capacity T and group size and
 // converts it; NULL means dense with every sequence holding T keys.
 int to_layout(const hga_kv_layout* in, int64_t T, int32_t group, hga::KvLayout* out) {
@@ -236,12 +332,8 @@ int hga_route_fresh_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   hga::KvLayout L;
   st = to_layout(layout, shape->seq_len, group, &L);
   if (st != HGA_OK) return st;
-  const bool fused = hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries) &&
-                     hga::row_route_can_refresh(shape->n_queries, chunk, group) &&
-                     !(dtype == HGA_BF16 &&
-                       hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
-                                              shape->n_queries, shape->head_dim));
-  if (!fused) {  // two launches: refresh, then route
+  if (!row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, false)) {
+    // two launches: refresh, then route
     st = summaries_common(K, dtype, layout, shape->batch, shape->kv_heads, shape->seq_len,
                           shape->head_dim, chunk, group, 0, 0, shape->n_queries, chunk_mean,
                           group_mean, stream);
@@ -274,39 +366,17 @@ static int route_impl(const hga_shape* shape, const hga_kv_layout* layout, const
                                               shape->n_queries, shape->seq_len, chunk, group,
                                               k_chunk, k_group);
   if (workspace_bytes < plan.bytes) return HGA_ERR_WORKSPACE;
-  hga::RouteArgs a{};
-  a.Q = Q;
-  a.chunk_mean = chunk_mean;
-  a.group_mean = group_mean;
-  a.B = static_cast<int>(shape->batch);
-  a.Hq = static_cast<int>(shape->q_heads);
-  a.Hkv = static_cast<int>(shape->kv_heads);
-  a.Nq = static_cast<int>(shape->n_queries);
-  a.T = static_cast<int>(shape->seq_len);
-  a.D = static_cast<int>(shape->head_dim);
-  a.C = chunk;
-  a.G = group;
-  a.gpc = chunk / group;
-  a.n_c = static_cast<int>((shape->seq_len + chunk - 1) / chunk);
-  a.n_g = static_cast<int>((shape->seq_len + group - 1) / group);
-  a.k_c = k_chunk;
-  a.k_g = k_group;
-  a.scale = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(shape->head_dim));
-  a.chunk_idx = chunk_idx;
-  a.group_idx = group_idx;
-  char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
-  a.chunk_scores = reinterpret_cast<float*>(ws + plan.off_chunk_scores);
-  a.group_scores = reinterpret_cast<float*>(ws + plan.off_group_scores);
-  a.split = plan.off_split ? reinterpret_cast<uint16_t*>(ws + plan.off_split) : nullptr;
-  a.seq_lens = layout ? layout->seq_lens : nullptr;
+  hga::RouteArgs a = route_args(shape, layout, Q, chunk_mean, group_mean, chunk, group, k_chunk,
+                                k_group, scale, chunk_idx, group_idx, workspace, plan);
   a.K = K_fresh;
   if (kv_fresh) a.kv = *kv_fresh;
   hipError_t e;
   if (a.split && hga::use_prefill_route(dtype, shape->q_heads, shape->kv_heads,
                                         shape->n_queries, shape->head_dim)) {
     e = hga::launch_route_prefill(a, as_stream(stream));
-  } else if (a.K || hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries)) {
+  } else if (a.K || hga::use_row_route(shape->batch, shape->q_heads, shape->n_queries,
+                                       shape->seq_len, shape->head_dim, chunk, group, k_chunk,
+                                       k_group, false)) {
     e = hga::launch_route_rows(a, dtype, as_stream(stream));
   } else {
     e = hga::launch_route(a, dtype, plan, as_stream(stream));
@@ -351,27 +421,80 @@ int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const voi
   const hga::AttendPlan plan = hga::plan_attend(rows, shape->head_dim, group, k_group);
   if (workspace_bytes < plan.bytes) return HGA_ERR_WORKSPACE;
   if (rows * plan.n_splits >= kMaxDim) return HGA_ERR_SHAPE;
-  hga::AttendArgs a{};
-  a.Q = Q;
-  a.K = K;
-  a.V = V;
-  a.group_idx = group_idx;
-  a.O = O;
-  a.lse = lse;
-  a.B = static_cast<int>(shape->batch);
-  a.Hq = static_cast<int>(shape->q_heads);
-  a.Hkv = static_cast<int>(shape->kv_heads);
-  a.Nq = static_cast<int>(shape->n_queries);
-  a.T = static_cast<int>(shape->seq_len);
-  a.D = static_cast<int>(shape->head_dim);
-  a.G = group;
-  a.k_g = k_group;
-  a.scale = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(shape->head_dim));
-  char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<unsigned*>(ws + plan.off_counters);
-  a.partials = reinterpret_cast<float*>(ws + plan.off_partials);
-  a.kv = L;
+  const hga::AttendArgs a = attend_args(shape, L, Q, K, V, group_idx, k_group, group, scale, O,
+                                        lse, workspace, plan);
   const hipError_t e = hga::launch_attend(a, dtype, plan, as_stream(stream));
+  return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
+}
+
+int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
+                                   int32_t k_chunk, int32_t k_group, size_t* bytes) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  *bytes = decode_workspace_bytes(shape, chunk, group, k_chunk, k_group);
+  return HGA_OK;
+}
+
+int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
+                               int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!one) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  *one = row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, true) ? 1 : 0;
+  return HGA_OK;
+}
+
+int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                       const void* K, const void* V, int32_t dtype, float* chunk_mean,
+                       float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+                       int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+                       void* O, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !chunk_mean || !group_mean || !group_idx || !O || !workspace)
+    return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  hga::KvLayout L;
+  st = to_layout(layout, shape->seq_len, group, &L);
+  if (st != HGA_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      !aligned16(chunk_mean) || !aligned16(group_mean) || !aligned16(workspace))
+    return HGA_ERR_LAYOUT;
+  if (workspace_bytes < decode_workspace_bytes(shape, chunk, group, k_chunk, k_group))
+    return HGA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  if (!row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, true)) {
+    // refresh + route, then attend
+    st = hga_route_fresh_ex(shape, layout, Q, K, dtype, chunk_mean, group_mean, chunk, group,
+                            k_chunk, k_group, scale, chunk_idx, group_idx, ws, workspace_bytes,
+                            stream);
+    if (st != HGA_OK) return st;
+    return hga_attend_ex(shape, layout, Q, K, V, dtype, group_idx, k_group, group, scale, O, lse,
+                         ws, workspace_bytes, stream);
+  }
+  const hga::RoutePlan rplan = hga::plan_route(shape->batch, shape->q_heads, shape->kv_heads,
+                                               shape->n_queries, shape->seq_len, chunk, group,
+                                               k_chunk, k_group);
+  const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
+  const hga::AttendPlan aplan = hga::plan_attend(rows, shape->head_dim, group, k_group, 8);
+  hga::RouteArgs ra = route_args(shape, layout, Q, chunk_mean, group_mean, chunk, group, k_chunk,
+                                 k_group, scale, chunk_idx, group_idx, ws, rplan);
+  ra.K = K;
+  ra.kv = L;
+  hga::AttendArgs aa = attend_args(shape, L, Q, K, V, group_idx, k_group, group, scale, O, lse,
+                                   ws, aplan);
+  aa.counters = reinterpret_cast<unsigned*>(ws) + kDecodeAttendCounters;
+  unsigned* ready = reinterpret_cast<unsigned*>(ws);  // the row route itself uses no counters
+  const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ready, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 

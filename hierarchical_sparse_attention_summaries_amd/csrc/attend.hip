@@ -1,253 +1,23 @@
 // Step 3 of HGA (abstract of "Hierarchical Global Attention (HGA)", arXiv
-// 2606.30709): exact token-level softmax attention over the routed tokens only.
-//
-// Each query row (b, h, i) owns k_group routed groups. A wave takes
-// `groups_per_wave` of them; for each group it gathers the group's keys and
-// values straight from HBM (a group is G contiguous rows of K and of V, read
-// with 16-byte coalesced loads, all loads of a 32-token tile issued before any
-// use) and folds them into an online softmax (running max m, sum l and output
-// o in fp32, exponentials in base 2 with log2(e) folded into the query). The
-// four waves of a workgroup merge in LDS; the workgroups of a row (split-K over
-// its groups) leave (m, l, o) partials and the last one to arrive merges them
-// and writes O and lse. HBM-bound: every routed K/V byte is read once.
+// 2606.30709): the exact-attention launch and its plan. The workgroup body
+// (gather + online softmax + split merge) is in hga_attend_body.h.
 #include <math.h>
 
+#include "hga_attend_body.h"
 #include "hga_device.h"
 #include "hga_internal.h"
 
 namespace hga {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kTile = 32;  // tokens per gather tile
-constexpr int kMaxSplits = 32;  // workgroups per row at most (the plan guarantees it)
+constexpr int kThreads = kAttendThreads;
+constexpr int kMaxSplits = kAttendMaxSplits;
 
 template <typename TKV, int D>
-__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
-                                                          int n_splits, int row_base) {
-  constexpr int EPL = Elem<TKV>::kPer16;
-  constexpr int LPR = D / EPL;        // lanes per token row
-  constexpr int RPL = kWave / LPR;    // token rows per wave-wide load
-  constexpr int NLD = kTile / RPL;    // loads per tile (per K and per V)
-  constexpr float kLog2e = 1.4426950408889634f;
-  constexpr float kLn2 = 0.6931471805599453f;
-
-  __shared__ float s_m[kWaves], s_l[kWaves];
-  __shared__ float s_o[kWaves][D];
-  __shared__ bool s_last;
-  __shared__ float s_part[kMaxSplits * (D + 2)];
-
-  const int row = row_base + static_cast<int>(blockIdx.x) / n_splits;
-  const int split = blockIdx.x % n_splits;
-  const int i = row % a.Nq;
-  const int bh = row / a.Nq;
-  const int h = bh % a.Hq;
-  const int b = bh / a.Hq;
-  const int kv = h / (a.Hq / a.Hkv);
-  const int p = seq_len_of(a.kv, b, a.T) - a.Nq + i;
-  const int t_lim = p + 1;  // tokens j <= p (p < the sequence's length <= T); none if p < 0
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int sub = lane / LPR;
-  const int col = (lane % LPR) * EPL;
-
-  const TKV* Kbase = static_cast<const TKV*>(a.K);
-  const TKV* Vbase = static_cast<const TKV*>(a.V);
-
-  float q[EPL];
-  {
-    widen(ld16(static_cast<const TKV*>(a.Q) + static_cast<size_t>(row) * D + col), q);
-    const float s = a.scale * kLog2e;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) q[e] *= s;
-  }
-
-  float m = -INFINITY, l = 0.f;
-  float o[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-
-  const int32_t* gl = a.group_idx + static_cast<size_t>(row) * a.k_g;
-  const int e0 = (split * kWaves + wave) * groups_per_wave;
-  const int e1 = min(e0 + groups_per_wave, a.k_g);
-  const int n_g = (a.T + a.G - 1) / a.G;
-
-  // Token range [t0, t1) of list entry e (empty for -1 padding, ids out of
-  // range, groups that start after the query, and pages out of range), and the
-  // element offset of its first row: the group's rows are consecutive.
-  auto span = [&](int e, int& t0, int& t1, int64_t& off) {
-    const int g = e < e1 ? gl[e] : -1;
-    t0 = t1 = 0;
-    off = 0;
-    if (g < 0 || g >= n_g) return;
-    const int s0 = g * a.G;
-    const int s1 = min(s0 + a.G, t_lim);
-    if (s1 <= s0) return;
-    off = kv_offset(a.kv, b, a.Hkv, kv, a.T, D, s0);
-    if (off < 0) return;
-    t0 = s0;
-    t1 = s1;
-  };
-  // Issue the loads of up to kTile tokens from `base` (rows >= t1 read as 0).
-  auto load = [&](int base, int t1, int64_t off, int t0, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int t = base + u * RPL + sub;
-      if (t < t1) {
-        const int64_t at = off + static_cast<int64_t>(t - t0) * D + col;  // row t of the group
-        kr[u] = ld16(Kbase + at);
-        vr[u] = ld16(Vbase + at);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  // Fold one loaded tile into (m, l, o). Token `base` must be valid.
-  auto consume = [&](int base, int t1, const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
-    float sc[NLD];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      float x[EPL];
-      widen(kr[u], x);
-      float d = 0.f;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) d = fmaf(q[k], x[k], d);
-      d = group_sum<LPR>(d);
-      sc[u] = (base + u * RPL + sub < t1) ? d : -INFINITY;
-      mt = fmaxf(mt, sc[u]);
-    }
-    mt = across_rows_max<LPR>(mt);
-    const float m_new = fmaxf(m, mt);  // finite: token `base` is valid
-    const float corr = exp2f(m - m_new);
-    l *= corr;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) o[k] *= corr;
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const float pu = exp2f(sc[u] - m_new);
-      l += pu;
-      float x[EPL];
-      widen(vr[u], x);
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) o[k] = fmaf(pu, x[k], o[k]);
-    }
-    m = m_new;
-  };
-
-  if (a.G <= kTile) {
-    // One tile per group. Two register buffers: the next group's keys and
-    // values are in flight while the current one is folded in.
-    uint4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
-    int a0, a1, b0, b1;
-    int64_t ao, bo;
-    span(e0, a0, a1, ao);
-    load(a0, a1, ao, a0, kA, vA);
-    for (int e = e0; e < e1; e += 2) {
-      span(e + 1, b0, b1, bo);
-      load(b0, b1, bo, b0, kB, vB);
-      if (a0 < a1) consume(a0, a1, kA, vA);
-      span(e + 2, a0, a1, ao);
-      load(a0, a1, ao, a0, kA, vA);
-      if (b0 < b1) consume(b0, b1, kB, vB);
-    }
-  } else {
-    // Groups longer than a tile: walk their tiles one by one.
-    uint4 kA[NLD], vA[NLD];
-    for (int e = e0; e < e1; ++e) {
-      int t0, t1;
-      int64_t off;
-      span(e, t0, t1, off);
-      for (int base = t0; base < t1; base += kTile) {
-        load(base, t1, off, t0, kA, vA);
-        consume(base, t1, kA, vA);
-      }
-    }
-  }
-  // Lanes of one column slot hold disjoint token rows: fold them.
-  l = across_rows_sum<LPR>(l);
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) o[k] = across_rows_sum<LPR>(o[k]);
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = l;
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) s_o[wave][col + k] = o[k];
-  }
-  __syncthreads();
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w]);
-  float Lsum = 0.f, acc = 0.f;
-  const int d = threadIdx.x;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(s_m[w] - M);
-      Lsum += s_l[w] * f;
-      if (d < D) acc += s_o[w][d] * f;
-    }
-  }
-
-  auto finish = [&](float Mx, float Lx, float ox) {
-    if (d < D) {
-      const float v = Lx > 0.f ? ox / Lx : 0.f;
-      const size_t off = static_cast<size_t>(row) * D + d;
-      if constexpr (sizeof(TKV) == 4) {
-        static_cast<float*>(a.O)[off] = v;
-      } else {
-        static_cast<uint16_t*>(a.O)[off] = static_cast<uint16_t>(bf16_bits(v));
-      }
-    }
-    if (a.lse && d == 0) a.lse[row] = Lx > 0.f ? (Mx + log2f(Lx)) * kLn2 : -INFINITY;
-  };
-
-  if (n_splits == 1) {
-    finish(M, Lsum, acc);
-    return;
-  }
-  float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
-  if (d < D) store_shared(part + 2 + d, acc);
-  if (d == 0) {
-    store_shared(part, M);
-    store_shared(part + 1, Lsum);
-  }
-  if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
-    return;
-
-  // Pull every split's (m, l, o) into LDS with all loads in flight at once.
-  const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
-  const int total = n_splits * (D + 2);
-  for (int base = 0; base < total; base += 4 * kThreads) {
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * kThreads + threadIdx.x;
-      v[u] = idx < total ? load_shared(rp + idx) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * kThreads + threadIdx.x;
-      if (idx < total) s_part[idx] = v[u];
-    }
-  }
-  __syncthreads();
-  float Mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, s_part[s * (D + 2)]);
-  float Lx = 0.f, ox = 0.f;
-  if (Mx != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float f = exp2f(s_part[s * (D + 2)] - Mx);
-      Lx += s_part[s * (D + 2) + 1] * f;
-      if (d < D) ox += s_part[s * (D + 2) + 2 + d] * f;
-    }
-  }
-  finish(Mx, Lx, ox);
+__global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
+                                                                int n_splits, int row_base) {
+  attend_body<TKV, D, false>(a, groups_per_wave, n_splits, row_base, static_cast<int>(blockIdx.x),
+                             nullptr);
 }
 
 template <typename TKV, int D>
@@ -271,7 +41,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g) {
+AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves) {
   AttendPlan pl{};
   // Enough waves to keep every CU's memory pipe busy (each wave keeps two
   // groups in flight), no more: larger groups_per_wave means fewer partials
@@ -280,11 +50,11 @@ AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g) {
   int gpw = 1;
   while (gpw < 16 && rows * ((k_g + 2 * gpw - 1) / (2 * gpw)) >= target_waves) gpw *= 2;
   (void)G;
-  // at most kMaxSplits workgroups (of kWaves waves) per row
-  while ((k_g + gpw - 1) / gpw > kMaxSplits * kWaves) gpw *= 2;
+  // at most kMaxSplits workgroups (of `waves` waves) per row
+  while ((k_g + gpw - 1) / gpw > kMaxSplits * waves) gpw *= 2;
   pl.groups_per_wave = gpw;
   const int waves_per_row = (k_g + gpw - 1) / gpw;
-  pl.n_splits = (waves_per_row + kWaves - 1) / kWaves;
+  pl.n_splits = (waves_per_row + waves - 1) / waves;
   pl.off_counters = 0;
   pl.off_partials = kCounterBytes;
   const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;

@@ -47,17 +47,53 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+
+// The values of lane l and of lane l ^ 16 (SPAN 16: the other row of a row
+// pair) or l ^ 32 (SPAN 32: the other half-wave), as (lower lane's, upper
+// lane's), via gfx950's permlane swaps: no LDS round trip.
+template <int SPAN>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  static_assert(SPAN == 16 || SPAN == 32, "row-pair or half-wave span");
+  if constexpr (SPAN == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  }
+}
+template <int SPAN>
+__device__ __forceinline__ float pair_sum(float v) {
+  uint32_t lo, hi;
+  lane_pair<SPAN>(__float_as_uint(v), lo, hi);
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+template <int SPAN>
+__device__ __forceinline__ float pair_max(float v) {
+  uint32_t lo, hi;
+  lane_pair<SPAN>(__float_as_uint(v), lo, hi);
+  return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+}
+
 // Sum over aligned groups of N lanes (N in 1,2,4,8,16,32,64); every lane of a
 // group gets the group's total. Within a 16-lane DPP row the butterfly is
-// quad xor1, quad xor2, half-row mirror, row mirror.
+// quad xor1, quad xor2, half-row mirror, row mirror; then row pairs and
+// half-waves.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
   if constexpr (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
   if constexpr (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
   if constexpr (N >= 16) v += dpp<0x140>(v);  // row_mirror
-  if constexpr (N >= 32) v += __shfl_xor(v, 16, kWave);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32, kWave);
+  if constexpr (N >= 32) v = pair_sum<16>(v);
+  if constexpr (N >= 64) v = pair_sum<32>(v);
   return v;
 }
 
@@ -66,15 +102,33 @@ __device__ __forceinline__ float group_sum(float v) {
 template <int S>
 __device__ __forceinline__ float across_rows_sum(float v) {
 #pragma unroll
-  for (int m = S; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  for (int m = S; m < 16; m <<= 1) v += __shfl_xor(v, m, kWave);
+  if constexpr (S <= 16) v = pair_sum<16>(v);
+  return pair_sum<32>(v);
 }
 template <int S>
 __device__ __forceinline__ float across_rows_max(float v) {
 #pragma unroll
-  for (int m = S; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  for (int m = S; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  if constexpr (S <= 16) v = pair_max<16>(v);
+  return pair_max<32>(v);
 }
+
+// Whole-wave sum of a 32-bit value; every lane gets the result.
+#define HGA_WAVE_REDUCE(NAME, OP)                                   \
+  __device__ __forceinline__ uint32_t NAME(uint32_t v) {            \
+    v = v OP dpp_u32<0xB1>(v);                                      \
+    v = v OP dpp_u32<0x4E>(v);                                      \
+    v = v OP dpp_u32<0x141>(v);                                     \
+    v = v OP dpp_u32<0x140>(v);                                     \
+    uint32_t lo, hi;                                                \
+    lane_pair<16>(v, lo, hi);                                       \
+    v = lo OP hi;                                                   \
+    lane_pair<32>(v, lo, hi);                                       \
+    return lo OP hi;                                                \
+  }
+HGA_WAVE_REDUCE(wave_add, +)
+#undef HGA_WAVE_REDUCE
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -102,19 +156,34 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // k items be present. All lanes of the wave must call it.
 template <int E>
 __device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) {
-  // Largest threshold t with #(key >= t) >= k, found bit by bit from the top:
-  // that is the k-th largest key. Stop early once exactly k keys are >= t: the
-  // chosen set is then fixed whatever the lower bits.
+  // The k-th largest key is the largest t with #(key >= t) >= k; it is found
+  // two bits per step from the top (the three candidate digits are counted
+  // independently; the threshold stays in scalar registers). Stop early once
+  // exactly k keys are >= t: the chosen set is then fixed whatever the lower
+  // bits.
   uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t t = thr | (1u << bit);
-    int cnt = 0;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t t1 = thr | (1u << bit), t2 = thr | (2u << bit), t3 = thr | (3u << bit);
+    int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) cnt += __popcll(ballot(key[e] >= t));
-    if (cnt >= k) {
-      thr = t;
-      if (cnt == k) break;
+    for (int e = 0; e < E; ++e) {
+      c1 += __popcll(ballot(key[e] >= t1));
+      c2 += __popcll(ballot(key[e] >= t2));
+      c3 += __popcll(ballot(key[e] >= t3));
     }
+    int c = -1;
+    if (c3 >= k) {
+      thr = t3;
+      c = c3;
+    } else if (c2 >= k) {
+      thr = t2;
+      c = c2;
+    } else if (c1 >= k) {
+      thr = t1;
+      c = c1;
+    }
+    thr = __builtin_amdgcn_readfirstlane(thr);
+    if (c == k) break;
   }
   int above = 0;
 #pragma unroll
@@ -144,6 +213,12 @@ __device__ __forceinline__ void store_shared(float* p, float v) {
 }
 __device__ __forceinline__ float load_shared(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared_i32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_shared_i32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Called by every thread of a workgroup after it issued its store_shared()

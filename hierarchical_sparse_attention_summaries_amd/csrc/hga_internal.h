@@ -99,18 +99,23 @@ bool use_prefill_route(int dtype, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 
 // Few query rows (small decode batches): one workgroup per row runs both
-// levels on-chip (no workspace use, no cross-workgroup hand-off).
-bool use_row_route(int64_t B, int64_t Hq, int64_t Nq);
+// levels on-chip (no workspace use, no cross-workgroup hand-off). Applies to
+// at most 1024 rows whose route fits a workgroup's LDS (plus extra_lds bytes
+// of other static LDS in the same kernel); `fresh`: the row route also
+// refreshes the newest chunks itself (a.K set), which needs Nq <= C and
+// C/G <= 16.
+bool use_row_route(int64_t B, int64_t Hq, int64_t Nq, int64_t T, int64_t D, int C, int G,
+                   int k_c, int k_g, bool fresh, size_t extra_lds = 0);
 hipError_t launch_route_rows(const RouteArgs& a, int dtype, hipStream_t stream);
-// Whether the row route can refresh the newest chunks itself (a.K set).
-bool row_route_can_refresh(int64_t Nq, int C, int G);
 
 struct AttendPlan {
   int groups_per_wave;
   int n_splits;         // workgroups per query row
   size_t off_counters, off_partials, bytes;
 };
-AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g);
+// `waves` per workgroup: 4 for the attention launch, 8 inside the fused
+// decode-step launch (whose workgroups are sized for routing).
+AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves = 4);
 
 struct AttendArgs {
   const void* Q;
@@ -128,6 +133,20 @@ struct AttendArgs {
 };
 hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
                          hipStream_t stream);
+
+// Decode step (refresh + route + attend) as one launch: routing workgroups
+// first, attention workgroups after them waiting on per-row ready flags.
+// Applies where the row route refreshes by itself with the attention's static
+// LDS (decode_step_lds) beside it, not in the prefill case; `ready` holds one
+// zero word per query row and is left zero.
+size_t decode_step_lds(int64_t D);
+// Whether every workgroup of the one-launch decode step is resident at once,
+// one per CU (small batches): routing never queues behind waiting attention,
+// and the big routing form applies.
+bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D, int G,
+                            int k_g);
+hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
+                              int dtype, unsigned* ready, hipStream_t stream);
 
 int device_cu_count();
 

@@ -238,6 +238,45 @@ int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const voi
                   int32_t k_group, int32_t group, float scale, void* O, float* lse,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes hga_decode_step_ex needs. As for every call here, the
+ * workspace's first 64 KiB must be zero before its first use and are left
+ * zero; the rest is scratch. */
+int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
+                                   int32_t k_chunk, int32_t k_group, size_t* bytes);
+
+/*
+ * One decode step, all three HGA steps (abstract: summaries, routing by
+ * summary, exact attention over the routed tokens): the same results as
+ * hga_route_fresh_ex followed by hga_attend_ex on the same arguments
+ * (chunk_idx, group_idx, chunk_mean and group_mean bit for bit; O and lse to
+ * fp32 rounding, the attention's partial sums being grouped differently).
+ *   Q [B, Hq, Nq, D]; K, V as the layout describes (NULL = dense, all T);
+ *   chunk_mean, group_mean: the summaries, whose chunks holding each
+ *   sequence's newest Nq keys are recomputed from K and written;
+ *   chunk_idx (or NULL), group_idx, O, lse (or NULL): written as by
+ *   hga_route_ex and hga_attend_ex.
+ * For small batches (hga_decode_step_one_launch: where hga_route_fresh_ex is
+ * one launch and every workgroup of the step fits the device at once, one per
+ * CU) the call is one launch: routing workgroups publish each row's group ids
+ * and a per-row flag in the workspace; attention workgroups of the same launch wait for the flag (a
+ * bounded wait; a row whose routing it does not see in time gets NaN in O and
+ * lse, and the workspace's first 64 KiB must then be zeroed before its next
+ * use) and the last one of each row clears it. Otherwise the two calls are
+ * enqueued. Calls that share a workspace must not overlap.
+ */
+/* Whether hga_decode_step_ex runs these arguments as one launch: *one = 1,
+ * else 0 (the calls it then enqueues are hga_route_fresh_ex and
+ * hga_attend_ex). */
+int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
+                               int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one);
+
+int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                       const void* K, const void* V, int32_t dtype, float* chunk_mean,
+                       float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+                       int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+                       void* O, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,33 @@ def test_paged_layout_rejected_before_launch():
     assert u(FAKE, ctypes.c_int32(1), ctypes.byref(ok), ctypes.c_int64(4), ctypes.c_int64(2),
              ctypes.c_int64(T), ctypes.c_int64(128), ctypes.c_int32(256), ctypes.c_int32(32),
              ctypes.c_int64(0), FAKE, FAKE, None) == PARAM          # newest < 1
+
+
+def test_decode_step_rejects_before_launch():
+    L = hga.lib()
+    n, nr, na = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    s = _shape()
+    assert L.hga_decode_step_workspace_size(ctypes.byref(s), 256, 32, 32, 64, ctypes.byref(n)) == OK
+    assert L.hga_route_workspace_size(ctypes.byref(s), 256, 32, 32, 64, ctypes.byref(nr)) == OK
+    assert L.hga_attend_workspace_size(ctypes.byref(s), 32, 64, ctypes.byref(na)) == OK
+    assert n.value >= max(nr.value, na.value)      # routing, then attention, in one workspace
+    d = L.hga_decode_step_ex
+    # shape, layout, Q, K, V, dtype, cm, gm, chunk, group, k_chunk, k_group, scale,
+    # chunk_idx, group_idx, O, lse, workspace, bytes, stream
+    args = [None, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 256, 32, 32, 64, 0.0, FAKE, FAKE, FAKE, None,
+            FAKE, n.value, None]
+    for i in (1, 2, 3, 5, 6, 13, 14, 16):             # Q, K, V, summaries, group_idx, O, workspace
+        bad = list(args); bad[i] = None
+        assert d(ctypes.byref(s), *bad) == NULL, i
+    bad = list(args); bad[4] = 9
+    assert d(ctypes.byref(s), *bad) == DTYPE
+    bad = list(args); bad[10] = 0
+    assert d(ctypes.byref(s), *bad) == PARAM
+    bad = list(args); bad[7] = 250
+    assert d(ctypes.byref(s), *bad) == PARAM
+    bad = list(args); bad[17] = n.value - 1
+    assert d(ctypes.byref(s), *bad) == WORKSPACE
+    bad = list(args); bad[3] = MIS
+    assert d(ctypes.byref(s), *bad) == LAYOUT
+    assert d(ctypes.byref(_shape(head_dim=96)), *args) == SHAPE
+    assert d(None, *args) == NULL

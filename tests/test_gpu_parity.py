@@ -418,3 +418,101 @@ def test_route_fresh_equals_update_then_route(case):
         O, lse = hga.attend(Q, Kc, Vc, g_fresh, w.group)
         torch.cuda.synchronize()
         check_workload(w, inp2, dict(cm=cm_f, gm=gm_f, cidx=cidx, gidx=g_fresh, O=O, lse=lse))
+
+
+def _bump_newest(w, Kc, layout_info):
+    """The newest keys of every sequence change after the summaries were built
+    (a decode step appended them)."""
+    if layout_info is None:
+        Kc[:, :, -w.Nq:] += 0.75
+    else:
+        seq_lens, table, page_tokens = layout_info
+        for b, Tb in enumerate(seq_lens):
+            for t in range(Tb - w.Nq, Tb):
+                Kc[int(table[b, t // page_tokens]), :, t % page_tokens] += 0.75
+
+
+def _same_attention(O_a, lse_a, O_b, lse_b, dtype):
+    """Two attention results over the same routed tokens whose fp32 partial
+    sums were grouped differently: equal to fp32 rounding, so bf16 outputs
+    differ by at most one bf16 step."""
+    a, b = O_a.float(), O_b.float()
+    d = (a - b).abs()
+    if dtype == "bf16":
+        lim = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 1e-6
+    else:
+        lim = torch.maximum(a.abs(), b.abs()) * 1e-5 + 1e-6
+    assert bool((d <= lim).all()), f"O differs by up to {float(d.max()):.3g}"
+    assert float((lse_a - lse_b).abs().max()) <= 1e-4
+
+
+DECODE_CASES = {
+    "bf16-b2-t8192-nq2": DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2),
+    "f32-b1-t4096": DECODE_64K.with_(B=1, T=4096, k_chunk=3, k_group=12, plants=1, dtype="f32"),
+    "bf16-paged-ragged": DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2),
+    "bf16-fallback-many-rows": DECODE_64K.with_(B=40, T=4096, k_chunk=2, k_group=4, plants=1),
+    "qwen3-b1-t65536": DECODE_64K,
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_step_equals_fresh_route_then_attend(case):
+    """hga_decode_step_ex (refresh + route + attend, one launch where the row
+    route applies) gives the summaries and routes of route_fresh_ex bit for
+    bit and the attention of attend_ex to fp32 rounding; on the dense case the
+    whole step also matches the oracle on the modified keys."""
+    w = DECODE_CASES[case]
+    log(f"case decode-step-{case} {w.name} B={w.B} T={w.T} Nq={w.Nq}")
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    layout, Kc, Vc, info = None, K, V, None
+    if "paged" in case:
+        seq_lens = [w.T, w.T - 100]
+        kp, vp, table, n_pages = _pages(w, inp, seq_lens, 64)
+        lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+        layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
+        Kc, Vc, info = kp, vp, (seq_lens, table, 64)
+    cm, gm = hga.build_summaries_ex(Kc, w.chunk, w.group, layout=layout, seq_len=w.T)
+    _bump_newest(w, Kc, info)
+    cm_d, gm_d = cm.clone(), gm.clone()
+    O_d, lse_d, c_d, g_d = hga.decode_step_ex(Q, Kc, Vc, cm_d, gm_d, w.T, w.chunk, w.group,
+                                              w.k_chunk, w.k_group, layout=layout)
+    cm_r, gm_r = cm.clone(), gm.clone()
+    c_r, g_r = hga.route_fresh_ex(Q, Kc, cm_r, gm_r, w.T, w.chunk, w.group, w.k_chunk,
+                                  w.k_group, layout=layout)
+    O_r, lse_r = hga.attend_ex(Q, Kc, Vc, g_r, w.group, layout=layout, seq_len=w.T)
+    torch.cuda.synchronize()
+    assert torch.equal(g_d, g_r) and torch.equal(c_d, c_r)
+    assert torch.equal(cm_d, cm_r) and torch.equal(gm_d, gm_r)
+    _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
+    if layout is None and w.T <= 8192:
+        from synth.inputs import Inputs
+        inp2 = Inputs(w, inp.seed, inp.Q, Kc.float().cpu().numpy(), inp.V)
+        check_workload(w, inp2, dict(cm=cm_d, gm=gm_d, cidx=c_d, gidx=g_d, O=O_d, lse=lse_d))
+
+
+def test_decode_step_back_to_back_leaves_counters_zero():
+    """Successive one-launch decode steps on one workspace (each step's queries
+    differ; only its counters are zero at the start) each match the two-call
+    result, and leave the counters at zero."""
+    log("case decode-step back-to-back")
+    # two attention workgroups per row, so the arrival counters are used too
+    w = DECODE_64K.with_(B=2, T=16384, k_chunk=8, k_group=64, plants=2)
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    cm, gm = hga.build_summaries(K, w.chunk, w.group)
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    nbytes = hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk, w.k_group)
+    # a workspace that an earlier call of another shape left dirty past its counters
+    ws = torch.full((nbytes + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws[:65536] = 0
+    for step in range(4):
+        Qs = (Q.float() * (1.0 + 0.25 * step)).to(Q.dtype) if step % 2 else Q.flip(1).contiguous()
+        O_d, lse_d, _, g_d = hga.decode_step_ex(Qs, K, V, cm, gm, w.T, w.chunk, w.group,
+                                                w.k_chunk, w.k_group, workspace=ws)
+        _, g_r = hga.route_fresh_ex(Qs, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
+        O_r, lse_r = hga.attend(Qs, K, V, g_r, w.group)
+        torch.cuda.synchronize()
+        assert torch.equal(g_d, g_r), step
+        _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
+        assert int(ws[:65536].count_nonzero()) == 0
