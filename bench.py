@@ -35,6 +35,8 @@ PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 SECONDARY = "qwen3-30b-a3b-decode-b16-t65536"   # the 64K point of the batch-16 context sweep
 HOST_TIER = "qwen3-30b-a3b-host-tier-b4-t262144"  # full K/V in pinned host memory
+PREFILL = "qwen3-30b-a3b-prefill-nq4096-t65536"     # 4096 new tokens against a 64K cache
+PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 
 def parse():
@@ -53,6 +55,8 @@ def parse():
                     help="skip the batch-16 64K-context point of the context sweep")
     ap.add_argument("--no-host-tier", action="store_true",
                     help="skip the 256K-context batch-4 run with K/V in pinned host memory")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 4096-query prefill step against a 64K cache (MFMA scoring)")
     return ap.parse_args()
 
 
@@ -125,6 +129,12 @@ def main():
         ht = measure(ALL[HOST_TIER], h_args, primary=False)
         out["host_tier"] = {k: ht[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
                                                "kernels_us", "host_tier")}
+    if not args.no_prefill and w.name != PREFILL:
+        p_args = argparse.Namespace(**vars(args))
+        p_args.steps, p_args.warmup = 5, 2
+        pf = measure(ALL[PREFILL], p_args, primary=False)
+        out["prefill"] = {k: pf[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
+                                             "kernels_us", "roofline", "roofline_step", "mfma")}
     if not args.no_secondary:
         w2 = ALL[SECONDARY]
         if w2.name != w.name:
@@ -171,31 +181,33 @@ def measure(w, args, primary: bool):
     rows = w.B * w.Hq * w.Nq
     gpc = w.chunk // w.group
 
-    def tokens_of(gg, p):
-        return max(0, min(gg * w.group + w.group, p + 1) - gg * w.group)
-
-    routed_tokens = 0
+    # tokens of group g usable by the query at position p (j <= p)
+    pos = (w.T - w.Nq + np.arange(w.Nq)).reshape(1, 1, w.Nq, 1)
+    ntok = np.clip(np.minimum(g * w.group + w.group, pos + 1) - g * w.group, 0, None)
+    ntok = np.where(g >= 0, ntok, 0)
+    routed_tokens = int(ntok.sum())
     union_tokens = 0      # K/V tokens routed to any query of a (sequence, KV head)
     union_cand = 0        # candidate group summaries read by any query of a (sequence, KV head)
     for b in range(w.B):
         for kv in range(w.Hkv):
-            seen = {}
-            cands = set()
-            for h in range(kv * r, (kv + 1) * r):
-                for i in range(w.Nq):
-                    p = w.T - w.Nq + i
-                    for gg in g[b, h, i]:
-                        if gg >= 0:
-                            n = tokens_of(int(gg), p)
-                            routed_tokens += n
-                            seen[int(gg)] = max(seen.get(int(gg), 0), n)
-                    for cc in c[b, h, i]:
-                        if cc >= 0:
-                            cands.update(int(cc) * gpc + j for j in range(gpc)
-                                         if int(cc) * gpc + j < w.n_groups)
-            union_tokens += sum(seen.values())
-            union_cand += len(cands)
-    attend_bytes = routed_tokens * w.D * 2 * esize + rows * (2 * w.D * esize + 4 * w.k_group + 4)
+            gs = g[b, kv * r:(kv + 1) * r].reshape(-1)
+            ns = ntok[b, kv * r:(kv + 1) * r].reshape(-1)
+            keep = gs >= 0
+            if keep.any():   # a group's usable tokens: its largest count over the queries
+                order = np.lexsort((-ns[keep], gs[keep]))
+                gk, nk = gs[keep][order], ns[keep][order]
+                first = np.ones(len(gk), dtype=bool)
+                first[1:] = gk[1:] != gk[:-1]
+                union_tokens += int(nk[first].sum())
+            cs = np.unique(c[b, kv * r:(kv + 1) * r].reshape(-1))
+            cs = cs[cs >= 0]
+            cand = (cs[:, None] * gpc + np.arange(gpc)[None, :]).reshape(-1)
+            union_cand += int((cand < w.n_groups).sum())
+    # Attention's algorithmic HBM bytes take each KV head's routed K/V once (the
+    # union over its queries); with many queries per head (prefill) most
+    # gathers then hit in cache, and the per-row gathers are reported apart.
+    attend_bytes = union_tokens * w.D * 2 * esize + rows * (2 * w.D * esize + 4 * w.k_group + 4)
+    gather_bytes = routed_tokens * w.D * 2 * esize
     # One decode step: Q, all chunk summaries, the candidate groups' summaries,
     # the routed K/V (union per KV head), O, lse and ids, plus the refresh of the
     # chunks holding the newest keys (their keys read, their summaries written).
@@ -382,9 +394,11 @@ def measure(w, args, primary: bool):
     if w.host_kv:
         kv_bytes = 2 * K0.numel() * esize
         hbm = sum(t.numel() * t.element_size() for t in (Q, cm0, gm0, O, lse, gidx0, ws_d))
+        # every row's routed groups cross the host link (no cache keeps host memory)
+        fetched = gather_bytes + rows * (2 * w.D * esize + 4 * w.k_group + 4)
         host = {"kv_bytes_in_host_memory": kv_bytes, "hbm_bytes_resident": hbm,
-                "fetched_bytes_per_token": attend_bytes // (w.B * w.Nq),
-                "host_link_gbs": round(attend_bytes / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
+                "fetched_bytes_per_token": fetched // (w.B * w.Nq),
+                "host_link_gbs": round(fetched / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
 
     def roof(kernel, nbytes, us):
         traffic, _ = stored_traffic(kernel, w.name)
@@ -397,8 +411,26 @@ def measure(w, args, primary: bool):
     # step's bytes. Beside it, the whole step (one launch for small batches)
     # against the step's algorithmic bytes.
     roofline = roof("attend", attend_bytes, attend_us)
+    roofline["gathered_bytes_per_launch"] = gather_bytes
+    roofline["gathered_gbs"] = round(gather_bytes / (attend_us * 1e-6) / 1e9, 1)
     roofline_step = roof("decode_step", step_bytes, decode_us)
     roofline_step["launches"] = 1 if decode_one_launch else 2
+
+    # Many queries per KV head (prefill): scoring is a dense MFMA contraction.
+    mfma = None
+    if w.Nq > 1 and w.dtype == "bf16" and (w.Hq // w.Hkv) * w.Nq >= 64:
+        rows_all = w.B * w.Hq * w.Nq
+        chunk_flops = 2 * w.D * w.n_chunks * rows_all                    # every chunk, every row
+        cand_flops = 2 * w.D * int((c >= 0).sum()) * gpc                  # the method's candidates
+        executed = 2 * (2 * w.D * (w.n_chunks + w.n_groups) * rows_all)   # dense, hi and lo passes
+        route_us = kern_us["route"]["avg"]
+        mfma = {"kernels": "route call: split + score_mfma + select",
+                "alg_flops": chunk_flops + cand_flops, "executed_flops": executed,
+                "route_us": round(route_us, 2),
+                "achieved_tflops_executed": round(executed / (route_us * 1e-6) / 1e12, 1),
+                "peak_tflops": PEAK_MFMA_BF16_TFLOPS,
+                "frac_executed": round(executed / (route_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                "note": "time of the whole route call, so a lower bound for the MFMA kernel alone"}
 
     # ---------------- CPU oracle baseline (host cores, bounded sample)
     cpu = None
@@ -439,6 +471,7 @@ def measure(w, args, primary: bool):
         out["quality_vs_dense"] = quality
     if host is not None:
         out["host_tier"] = host
+    out["mfma"] = mfma
     del sets, graphs_keep
     return out
 

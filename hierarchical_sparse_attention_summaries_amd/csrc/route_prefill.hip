@@ -24,6 +24,8 @@
 #include "hga_internal.h"
 #include "hga_select.h"
 
+#include <stdint.h>
+
 namespace hga {
 namespace {
 
@@ -195,6 +197,311 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(RouteArgs a, int n
   }
 }
 
+// ---------------------------------------------------------------------------
+// Both levels in one kernel, scores never leaving the chip. A workgroup of
+// kFusedThreads / 64 waves owns kFusedRows head-major query rows of one
+// (sequence, KV head):
+//  1. MFMA scores of the 32 rows against every chunk summary -> LDS;
+//  2. each wave selects the chunks of its rows (chunk 0, the row's own chunk L,
+//     the k_chunk best between) and marks, per row, each kept chunk's rank;
+//  3. MFMA scores against every group summary; a score is kept only if its
+//     group lies in a kept chunk of that row (and starts at or before the row's
+//     position), and goes straight to the row's candidate slot in LDS (the slot
+//     of chunk rank x C/G + group within chunk: candidates in ascending group
+//     order, as the selection expects);
+//  4. each wave selects the groups of its rows and writes the ids.
+// Same scores (same MFMA order) and same selection as the three-kernel path.
+constexpr int kFusedRows = 32;
+constexpr int kFusedBlocks = kFusedRows / 16;  // 16-row MFMA blocks
+constexpr int kFusedThreads = 256;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+
+struct FusedLds {
+  int stride;  // floats per row of the score area
+  size_t scores, kept, rank, bytes;
+};
+__host__ __device__ inline FusedLds fused_lds(int n_c, int cap, int gpc) {
+  FusedLds f{};
+  f.stride = n_c > cap * gpc ? n_c : cap * gpc;
+  f.scores = 0;
+  f.kept = f.scores + static_cast<size_t>(kFusedRows) * f.stride * 4;
+  f.rank = f.kept + static_cast<size_t>(kFusedRows) * cap * 4;
+  f.bytes = f.rank + static_cast<size_t>(kFusedRows) * ((n_c + 3) / 4 * 4);
+  return f;
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin by index. Each XCD takes a
+// contiguous share of the (sequence, KV head, row tile) list, so that one
+// (sequence, KV head)'s split summaries (1.2 MB at 64K, read by every tile of
+// it) stay in one or two XCDs' L2 instead of all eight.
+__host__ __device__ inline int64_t fused_tiles_per_xcd(int64_t total) { return (total + 7) / 8; }
+
+template <int D, int E>
+__global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(RouteArgs a,
+                                                                            int n_row_tiles,
+                                                                            int gpc_shift) {
+  constexpr int KS = D / 32;
+  constexpr int W = kFusedWaves;
+  extern __shared__ float s_lds[];
+  const int cap = kept_capacity(a);
+  const FusedLds lay = fused_lds(a.n_c, cap, a.gpc);
+  float* s_sc = s_lds;
+  int* s_kept = reinterpret_cast<int*>(reinterpret_cast<char*>(s_lds) + lay.kept);
+  uint8_t* s_rank = reinterpret_cast<uint8_t*>(s_lds) + lay.rank;
+  const int rank_stride = (a.n_c + 3) / 4 * 4;
+  __shared__ int s_nk[kFusedRows];
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int lr = lane % 16;
+  const int lk = lane / 16;
+  const int64_t total = static_cast<int64_t>(a.B) * a.Hkv * n_row_tiles;
+  const int64_t tile = (blockIdx.x % 8) * fused_tiles_per_xcd(total) + blockIdx.x / 8;
+  if (tile >= total) return;  // whole workgroup: no barrier follows
+  const int rt = static_cast<int>(tile % n_row_tiles);
+  const int bkv = static_cast<int>(tile / n_row_tiles);
+  const int kv = bkv % a.Hkv;
+  const int b = bkv / a.Hkv;
+  const int r = a.Hq / a.Hkv;
+  const int M = r * a.Nq;
+  const int N = a.n_c + a.n_g;
+  const size_t row0 = static_cast<size_t>(b * a.Hq + kv * r) * a.Nq;
+  const int rho0 = rt * kFusedRows;
+  const int nrows = min(kFusedRows, M - rho0);
+  const int Tb = route_seq_len(a, b);
+  const int gmask = a.gpc - 1;
+  auto pos_of = [&](int t) { return Tb - a.Nq + (rho0 + t) % a.Nq; };  // tile row -> p
+  auto wrow_of = [&](int t) {  // tile row -> workspace row (b, h, i)
+    const int rho = rho0 + t;
+    return row0 + static_cast<size_t>(rho / a.Nq) * a.Nq + rho % a.Nq;
+  };
+
+  constexpr int RB = kFusedBlocks;
+  uint4 qa[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rho = rho0 + rb * 16 + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[rb][ks] = rho < M ? ld16(static_cast<const uint16_t*>(a.Q) + (row0 + rho) * D + ks * 32 +
+                                  lk * 8)
+                           : make_uint4(0, 0, 0, 0);
+  }
+  const uint16_t* hi_base = a.split + static_cast<size_t>(bkv) * 2 * N * D;
+  const uint16_t* lo_base = hi_base + static_cast<size_t>(N) * D;
+  auto load_b = [&](int col, int limit, uint4 (&h)[KS], uint4 (&l)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (col < limit) {
+        h[ks] = ld16(hi_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
+        l[ks] = ld16(lo_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
+      } else {
+        h[ks] = make_uint4(0, 0, 0, 0);
+        l[ks] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto mfma = [&](const uint4 (&h)[KS], const uint4 (&l)[KS], f32x4 (&acc)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][ks]), as_bf16x8(h[ks]),
+                                                          acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][ks]), as_bf16x8(l[ks]),
+                                                          acc[rb], 0, 0, 0);
+      }
+    }
+  };
+  // 16-column blocks of summary rows [col0, limit): this wave takes blocks
+  // wave, wave + W, ...; the next block's operands load while one runs.
+  // consume(first column, acc): lane holds rows rb*16 + lk*4 + i, column + lr.
+  auto sweep = [&](int col0, int limit, auto&& consume) {
+    const int nblk = (limit - col0 + 15) / 16;
+    uint4 hA[KS], lA[KS], hB[KS], lB[KS];
+    f32x4 acc[RB];
+    int cb = wave;
+    if (cb < nblk) load_b(col0 + cb * 16 + lr, limit, hA, lA);
+    for (; cb < nblk; cb += 2 * W) {
+      if (cb + W < nblk) load_b(col0 + (cb + W) * 16 + lr, limit, hB, lB);
+      mfma(hA, lA, acc);
+      consume(col0 + cb * 16, acc);
+      if (cb + W >= nblk) break;
+      if (cb + 2 * W < nblk) load_b(col0 + (cb + 2 * W) * 16 + lr, limit, hA, lA);
+      mfma(hB, lB, acc);
+      consume(col0 + (cb + W) * 16, acc);
+    }
+  };
+
+  // 1. chunk scores
+  sweep(0, a.n_c, [&](int c0, const f32x4 (&acc)[RB]) {
+    const int c = c0 + lr;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = rb * 16 + lk * 4 + i;
+        if (t < nrows && c < a.n_c) s_sc[t * lay.stride + c] = acc[rb][i] * a.scale;
+      }
+  });
+  __syncthreads();
+
+  // 2. chunk selection, 8 rows per wave
+  for (int t = wave; t < nrows; t += W) {
+    const int p = pos_of(t);
+    int* kept = s_kept + t * cap;
+    uint8_t* rank = s_rank + t * rank_stride;
+    for (int c = lane; c < a.n_c; c += kWave) rank[c] = 0xFF;
+    int n_kept = 0;
+    if (p >= 0) {
+      const int L = p / a.C;
+      const float* cs = s_sc + t * lay.stride;
+      if (L + 1 <= a.k_c + 2) {
+        n_kept = L + 1;
+        for (int c = lane; c < n_kept; c += kWave) kept[c] = c;
+      } else {
+        n_kept = a.k_c + 2;
+        if (a.k_c > 0) {
+          uint32_t key[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int u = e * kWave + lane;
+            key[e] = u < L - 1 ? order_key(cs[1 + u]) : 0u;
+          }
+          const uint32_t chosen = wave_top_k<E>(key, a.k_c);
+          int before = 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const bool ch = (chosen >> e) & 1u;
+            const uint64_t m = ballot(ch);
+            if (ch) kept[1 + before + bits_below(m)] = 1 + e * kWave + lane;
+            before += __popcll(m);
+          }
+        }
+        if (lane == 0) {
+          kept[0] = 0;
+          kept[n_kept - 1] = L;
+        }
+      }
+    }
+    wave_lds_sync();
+    for (int u = lane; u < n_kept; u += kWave) rank[kept[u]] = static_cast<uint8_t>(u);
+    if (a.chunk_idx) {
+      int32_t* out = a.chunk_idx + wrow_of(t) * (a.k_c + 2);
+      for (int u = lane; u < a.k_c + 2; u += kWave) out[u] = u < n_kept ? kept[u] : -1;
+    }
+    if (lane == 0) s_nk[t] = n_kept;
+  }
+  __syncthreads();
+
+  // 3. group scores, straight into each row's candidate slots. A lane's
+  // accumulator rows are fixed: their last usable group (-1 for rows past the
+  // tile) is worked out once.
+  int g_last[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = rb * 16 + lk * 4 + i;
+      const int p = t < nrows ? pos_of(t) : -1;
+      g_last[rb][i] = p >= 0 ? p / a.G : -1;
+    }
+  sweep(a.n_c, N, [&](int c0, const f32x4 (&acc)[RB]) {
+    const int g = c0 + lr - a.n_c;
+    if (g >= a.n_g) return;
+    const int c = g >> gpc_shift;
+    const int slot = g & gmask;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = rb * 16 + lk * 4 + i;
+        if (g <= g_last[rb][i]) {
+          const int rk = s_rank[t * rank_stride + c];
+          if (rk != 0xFF) s_sc[t * lay.stride + (rk << gpc_shift) + slot] = acc[rb][i] * a.scale;
+        }
+      }
+  });
+  __syncthreads();
+
+  // 4. group selection: candidates after p (or past the end) sit only at the
+  // end of a row's list, in its last kept chunk
+  for (int t = wave; t < nrows; t += W) {
+    const int p = pos_of(t);
+    const int n_kept = s_nk[t];
+    const int* kept = s_kept + t * cap;
+    const int n_cand = n_kept * a.gpc;
+    auto gid = [&](int u) { return (kept[u >> gpc_shift] << gpc_shift) + (u & gmask); };
+    int n_valid = 0;
+    for (int u = lane; u < n_cand; u += kWave) {
+      const int g = gid(u);
+      n_valid += (g < a.n_g && static_cast<int64_t>(g) * a.G <= p) ? 1 : 0;
+    }
+    n_valid = static_cast<int>(wave_add(static_cast<uint32_t>(n_valid)));
+    const float* gs = s_sc + t * lay.stride;
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int u = e * kWave + lane;
+      key[e] = u < n_valid ? order_key(gs[u]) : 0u;
+    }
+    uint32_t chosen = 0;
+    if (n_valid <= a.k_g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) chosen |= static_cast<uint32_t>(key[e] != 0u) << e;
+    } else {
+      chosen = wave_top_k<E>(key, a.k_g);
+    }
+    int32_t* out = a.group_idx + wrow_of(t) * a.k_g;
+    int before = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ch = (chosen >> e) & 1u;
+      const uint64_t m = ballot(ch);
+      if (ch) out[before + bits_below(m)] = gid(e * kWave + lane);
+      before += __popcll(m);
+    }
+    for (int u = before + lane; u < a.k_g; u += kWave) out[u] = -1;
+  }
+}
+
+template <int D>
+hipError_t launch_fused_d(const RouteArgs& a, int n_row_tiles, int gpc_shift, size_t lds,
+                          hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.B) * a.Hkv * n_row_tiles;
+  const dim3 grid(static_cast<unsigned>(8 * fused_tiles_per_xcd(total)));
+  switch (select_regs(a)) {
+#define HGA_FUSED_CASE(EV)                                                                       \
+  case EV: {                                                                                     \
+    const void* f = reinterpret_cast<const void*>(&route_prefill_fused_kernel<D, EV>);           \
+    if (lds > 65536) {                                                                           \
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,    \
+                                               static_cast<int>(lds));                           \
+      if (e != hipSuccess) return e;                                                             \
+    }                                                                                            \
+    hipLaunchKernelGGL((route_prefill_fused_kernel<D, EV>), grid, dim3(kFusedThreads), lds,      \
+                       stream, a, n_row_tiles, gpc_shift);                                       \
+    break;                                                                                       \
+  }
+    HGA_FUSED_CASE(1)
+    HGA_FUSED_CASE(2)
+    HGA_FUSED_CASE(3)
+    HGA_FUSED_CASE(4)
+    HGA_FUSED_CASE(5)
+    HGA_FUSED_CASE(6)
+    HGA_FUSED_CASE(8)
+    HGA_FUSED_CASE(16)
+    HGA_FUSED_CASE(32)
+    HGA_FUSED_CASE(64)
+#undef HGA_FUSED_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 
@@ -216,6 +523,16 @@ bool use_prefill_route(int dtype, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D
   return dtype == kBF16 && (Hq / Hkv) * Nq >= 64;
 }
 
+// The one-kernel form needs a power-of-two C/G (shifts), kept-chunk ranks
+// below 255 (one byte each) and its LDS within a workgroup's 160 KiB.
+constexpr size_t kMaxWorkgroupLds = 160 * 1024;
+bool fused_prefill_ok(const RouteArgs& a) {
+  if ((a.gpc & (a.gpc - 1)) != 0) return false;
+  const int cap = kept_capacity(a);
+  if (cap >= 255) return false;
+  return fused_lds(a.n_c, cap, a.gpc).bytes + 256 <= kMaxWorkgroupLds;
+}
+
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream) {
   const int r = a.Hq / a.Hkv;
   const int M = r * a.Nq;
@@ -225,6 +542,14 @@ hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((split_kernel<64>), split_grid, dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL((split_kernel<128>), split_grid, dim3(kThreads), 0, stream, a);
+  }
+  if (fused_prefill_ok(a)) {
+    int shift = 0;
+    while ((1 << shift) < a.gpc) ++shift;
+    const int n_row_tiles = (M + kFusedRows - 1) / kFusedRows;
+    const size_t lds = fused_lds(a.n_c, kept_capacity(a), a.gpc).bytes;
+    return a.D == 64 ? launch_fused_d<64>(a, n_row_tiles, shift, lds, stream)
+                     : launch_fused_d<128>(a, n_row_tiles, shift, lds, stream);
   }
   const int n_row_tiles = (M + kTileRows - 1) / kTileRows;
   const int n_col_tiles = (N + kTileCols - 1) / kTileCols;

@@ -72,6 +72,8 @@ PREFILL_SMALL = [
     Workload("prefill-small", 1, 8, 2, 128, 4096, 100, 128, 32, 4, 8, 1e6, "bf16", 2),
     Workload("prefill-d64-ragged", 2, 4, 1, 64, 2000, 64, 64, 16, 6, 10, 1e4, "bf16", 0),
     Workload("prefill-gpc1-mha", 1, 2, 2, 128, 1500, 70, 32, 32, 5, 5, 1e4, "bf16", 0),
+    # C/G not a power of two: the three-kernel form (scores through the workspace)
+    Workload("prefill-gpc3", 1, 8, 2, 128, 3000, 100, 96, 32, 4, 8, 1e4, "bf16", 0),
 ]
 
 
@@ -516,3 +518,28 @@ def test_decode_step_back_to_back_leaves_counters_zero():
         assert torch.equal(g_d, g_r), step
         _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
         assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_prefill_ragged_with_queries_before_the_first_key():
+    """Prefill (MFMA route) over a ragged batch: the shortest sequence holds
+    fewer keys than there are new queries, so its first queries route to
+    nothing; every other query matches the oracle run on its own sequence."""
+    log("case prefill-ragged")
+    w = Workload("prefill-ragged", 3, 8, 2, 128, 2048, 40, 128, 32, 3, 6, 1e4, "bf16", 0)
+    seq_lens = [2048, 1000, 25]
+    inp = generate(w)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    out = _run_ragged(w, inp, seq_lens, hga.Layout(seq_lens=lens), to_dev(inp.K, w.dtype),
+                      to_dev(inp.V, w.dtype))
+    from synth.inputs import Inputs
+    from tests.gpu_runner import check_ragged
+    check_ragged(w.with_(B=2), inp, seq_lens[:2], {k: v[:2] for k, v in out.items()})
+    Tb, short = seq_lens[2], w.Nq - seq_lens[2]          # queries 0..short-1 sit before key 0
+    assert (out["gidx"][2, :, :short] == -1).all() and (out["cidx"][2, :, :short] == -1).all()
+    assert (out["O"][2, :, :short] == 0).all() and torch.isinf(out["lse"][2, :, :short]).all()
+    wb = w.with_(B=1, T=Tb, Nq=Tb)
+    sub = Inputs(wb, inp.seed, inp.Q[2:3, :, short:], inp.K[2:3, :, :Tb], inp.V[2:3, :, :Tb])
+    ob = dict(cm=out["cm"][2:3, :, :wb.n_chunks], gm=out["gm"][2:3, :, :wb.n_groups],
+              cidx=out["cidx"][2:3, :, short:], gidx=out["gidx"][2:3, :, short:],
+              O=out["O"][2:3, :, short:], lse=out["lse"][2:3, :, short:])
+    check_workload(wb, sub, ob)
