@@ -57,6 +57,8 @@ def parse():
                     help="skip the 256K-context batch-4 run with K/V in pinned host memory")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 4096-query prefill step against a 64K cache (MFMA scoring)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the batch-16 context sweep below 64K (4096..32768 tokens)")
     return ap.parse_args()
 
 
@@ -135,6 +137,23 @@ def main():
         pf = measure(ALL[PREFILL], p_args, primary=False)
         out["prefill"] = {k: pf[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
                                              "kernels_us", "roofline", "roofline_step", "mfma")}
+    if not args.no_sweep:
+        # the batch-16 context sweep; its 64K point is the secondary run below
+        from synth import SWEEP
+        s_args = argparse.Namespace(**vars(args))
+        s_args.steps, s_args.warmup = 40, 10
+        out["sweep"] = []
+        for T in sorted(SWEEP):
+            ws = SWEEP[T]
+            if ws.name in (w.name, SECONDARY):
+                continue
+            r = measure(ws, s_args, primary=False)
+            out["sweep"].append({"seq_len": T, "value": r["value"], "unit": r["unit"],
+                                 "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+                                 "attend_gbs": r["roofline"]["achieved"],
+                                 "attend_frac": r["roofline"]["frac"],
+                                 "step_gbs": r["roofline_step"]["achieved"],
+                                 "kernels_us": r["kernels_us"]})
     if not args.no_secondary:
         w2 = ALL[SECONDARY]
         if w2.name != w.name:

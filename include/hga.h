@@ -219,8 +219,8 @@ int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void
 
 /* Decode-step form of step 1 + step 2: hga_update_summaries_ex(newest = Nq)
  * followed by hga_route_ex, with the same results bit for bit. For small
- * batches (B*Hq*Nq <= 1024, Nq <= chunk, chunk/group <= 16, not the MFMA
- * prefill case) it runs as one launch: each routing workgroup recomputes the
+ * batches (B*Hq*Nq <= 1024, Nq <= chunk, chunk/group <= 16, the routing
+ * state within 64 KiB of LDS, not the MFMA prefill case) it runs as one launch: each routing workgroup recomputes the
  * newest chunks of its sequence from K, writes them to chunk_mean/group_mean
  * and scores with them; otherwise it enqueues the two calls. K is the cache the
  * layout describes. Workspace as hga_route_workspace_size. */
@@ -258,8 +258,8 @@ int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_
  * For small batches (hga_decode_step_one_launch: where hga_route_fresh_ex is
  * one launch and every workgroup of the step fits the device at once, one per
  * CU) the call is one launch: routing workgroups publish each row's group ids
- * and a per-row flag in the workspace; attention workgroups of the same launch wait for the flag (a
- * bounded wait; a row whose routing it does not see in time gets NaN in O and
+ * and a per-row flag in the workspace; attention workgroups of the same
+ * launch wait for the flag (a bounded wait; a row whose routing it does not see in time gets NaN in O and
  * lse, and the workspace's first 64 KiB must then be zeroed before its next
  * use) and the last one of each row clears it. Otherwise the two calls are
  * enqueued. Calls that share a workspace must not overlap.
