@@ -244,6 +244,12 @@ int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const voi
 int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
                                    int32_t k_chunk, int32_t k_group, size_t* bytes);
 
+/* Whether hga_decode_step_ex runs these arguments as one launch: *one = 1,
+ * else 0 (the calls it then enqueues are hga_route_fresh_ex and
+ * hga_attend_ex). */
+int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
+                               int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one);
+
 /*
  * One decode step, all three HGA steps (abstract: summaries, routing by
  * summary, exact attention over the routed tokens): the same results as
@@ -259,17 +265,11 @@ int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_
  * one launch and every workgroup of the step fits the device at once, one per
  * CU) the call is one launch: routing workgroups publish each row's group ids
  * and a per-row flag in the workspace; attention workgroups of the same
- * launch wait for the flag (a bounded wait; a row whose routing it does not see in time gets NaN in O and
- * lse, and the workspace's first 64 KiB must then be zeroed before its next
- * use) and the last one of each row clears it. Otherwise the two calls are
+ * launch wait for the flag (a bounded wait; a row whose routing it does not
+ * see in time gets NaN in O and lse, and the workspace's first 64 KiB must
+ * then be zeroed before its next use) and the last one of each row clears it. Otherwise the two calls are
  * enqueued. Calls that share a workspace must not overlap.
  */
-/* Whether hga_decode_step_ex runs these arguments as one launch: *one = 1,
- * else 0 (the calls it then enqueues are hga_route_fresh_ex and
- * hga_attend_ex). */
-int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
-                               int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one);
-
 int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
                        const void* K, const void* V, int32_t dtype, float* chunk_mean,
                        float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
