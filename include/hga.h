@@ -267,8 +267,9 @@ int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t ch
  * and a per-row flag in the workspace; attention workgroups of the same
  * launch wait for the flag (a bounded wait; a row whose routing it does not
  * see in time gets NaN in O and lse, and the workspace's first 64 KiB must
- * then be zeroed before its next use) and the last one of each row clears it. Otherwise the two calls are
- * enqueued. Calls that share a workspace must not overlap.
+ * then be zeroed before its next use) and the last one of each row clears
+ * it. Otherwise the two calls are enqueued. Calls that share a workspace must
+ * not overlap.
  */
 int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
                        const void* K, const void* V, int32_t dtype, float* chunk_mean,
