@@ -159,7 +159,7 @@ size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, 
                                    chunk, group, k_chunk, k_group)
                        .bytes,
                    hga::plan_attend(rows, s->head_dim, group, k_group).bytes,
-                   hga::plan_attend(rows, s->head_dim, group, k_group, 8).bytes});
+                   hga::plan_decode_attend(rows, s->head_dim, k_group).bytes});
 }
 
 // Checks a caller's K/V layout against the capacity T and group size and
@@ -485,7 +485,7 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
                                                shape->n_queries, shape->seq_len, chunk, group,
                                                k_chunk, k_group);
   const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
-  const hga::AttendPlan aplan = hga::plan_attend(rows, shape->head_dim, group, k_group, 8);
+  const hga::AttendPlan aplan = hga::plan_decode_attend(rows, shape->head_dim, k_group);
   hga::RouteArgs ra = route_args(shape, layout, Q, chunk_mean, group_mean, chunk, group, k_chunk,
                                  k_group, scale, chunk_idx, group_idx, ws, rplan);
   ra.K = K;

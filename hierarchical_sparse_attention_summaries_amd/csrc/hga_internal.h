@@ -140,6 +140,8 @@ hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
 // LDS (decode_step_lds) beside it, not in the prefill case; `ready` holds one
 // zero word per query row and is left zero.
 size_t decode_step_lds(int64_t D);
+// Attention plan inside the one-launch decode step (8 waves per workgroup).
+AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g);
 // Whether every workgroup of the one-launch decode step is resident at once,
 // one per CU (small batches): routing never queues behind waiting attention,
 // and the big routing form applies.
