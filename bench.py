@@ -131,6 +131,7 @@ def main():
         ht = measure(ALL[HOST_TIER], h_args, primary=False)
         out["host_tier"] = {k: ht[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
                                                "kernels_us", "host_tier")}
+        out["host_tier"]["step"] = "route_fresh_ex + attend_staged (distinct routed groups staged once)"
     if not args.no_prefill and w.name != PREFILL:
         p_args = argparse.Namespace(**vars(args))
         p_args.steps, p_args.warmup = 5, 2
@@ -291,6 +292,25 @@ def measure(w, args, primary: bool):
     step = k_decode
     decode_one_launch = hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk,
                                                    w.k_group)
+    if w.host_kv:
+        # K/V in host memory: route (refreshing from host K), then copy each
+        # (sequence, KV head)'s distinct routed groups into a device pool once
+        # and attend from it
+        pages, st_bytes = hga.attend_staged_sizes(shape, w.group, w.k_group)
+        ws_st = torch.zeros(st_bytes, dtype=torch.uint8, device=dev)
+        pools = tuple(torch.empty(pages * w.group * w.D, dtype=tdt, device=dev) for _ in range(2))
+
+        def k_attend_staged(s):
+            K, V, cm, gm = sets[s]
+            hga.attend_staged(Q, K, V, gidx, w.group, out=O, lse=lse, pools=pools,
+                              workspace=ws_st)
+
+        def k_decode(s):
+            k_route_fresh(s)
+            k_attend_staged(s)
+
+        step = k_decode
+        decode_one_launch = False
 
     if args.only:
         fn = {"attend": k_attend, "route": k_route, "update": k_update, "step": step,
@@ -388,8 +408,11 @@ def measure(w, args, primary: bool):
     # launches of one kernel (rotating over the copies), the GPU kept busy
     # while the host enqueues; average = elapsed / n.
     n_k = max(50, min(args.steps, 400))
-    names = ("decode_step", "route_fresh", "attend", "update", "route")   # the step is the first
-    fns = (k_decode, k_route_fresh, k_attend, k_update, k_route)
+    names = ["decode_step", "route_fresh", "attend", "update", "route"]   # the step is the first
+    fns = [k_decode, k_route_fresh, k_attend, k_update, k_route]
+    if w.host_kv:
+        names.append("attend_staged")
+        fns.append(k_attend_staged)
     kern_us = {}
     for nm, fn in zip(names, fns):
         reps = []
@@ -412,12 +435,18 @@ def measure(w, args, primary: bool):
     host = None
     if w.host_kv:
         kv_bytes = 2 * K0.numel() * esize
-        hbm = sum(t.numel() * t.element_size() for t in (Q, cm0, gm0, O, lse, gidx0, ws_d))
-        # every row's routed groups cross the host link (no cache keeps host memory)
-        fetched = gather_bytes + rows * (2 * w.D * esize + 4 * w.k_group + 4)
+        hbm = sum(t.numel() * t.element_size()
+                  for t in (Q, cm0, gm0, O, lse, gidx0, ws_d, ws_st, *pools))
+        # staged: each (sequence, KV head)'s distinct routed groups cross the
+        # host link once; direct: every row's groups do
+        fetched = union_tokens * w.D * 2 * esize
+        direct = gather_bytes
         host = {"kv_bytes_in_host_memory": kv_bytes, "hbm_bytes_resident": hbm,
                 "fetched_bytes_per_token": fetched // (w.B * w.Nq),
-                "host_link_gbs": round(fetched / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
+                "host_link_gbs": round(fetched / (kern_us["attend_staged"]["avg"] * 1e-6) / 1e9, 2),
+                "direct_fetched_bytes_per_token": direct // (w.B * w.Nq),
+                "direct_attend_us": round(kern_us["attend"]["avg"], 1),
+                "direct_host_link_gbs": round(direct / (kern_us["attend"]["avg"] * 1e-6) / 1e9, 2)}
 
     def roof(kernel, nbytes, us):
         traffic, _ = stored_traffic(kernel, w.name)

@@ -107,6 +107,9 @@ def _load():
         "hga_route_fresh_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, i32, vp, vp, i32, i32,
                                               i32, i32, f32, vp, vp, vp, sz, vp]),
         "hga_decode_step_workspace_size": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, P(sz)]),
+        "hga_attend_staged_sizes": (ctypes.c_int, [P(Shape), i32, i32, P(i64), P(sz)]),
+        "hga_attend_staged": (ctypes.c_int, [P(Shape), vp, vp, vp, i32, vp, i32, i32, f32, vp, vp,
+                                             vp, vp, i64, vp, sz, vp]),
         "hga_decode_step_one_launch": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, i32, P(i32)]),
         "hga_decode_step_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, vp, i32,
                                               i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
@@ -463,3 +466,44 @@ def decode_step_ex(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chu
                                    _ptr(out), _ptr(lse if want_lse else None), _ptr(ws),
                                    ws.numel(), _stream(Q.device)), "hga_decode_step_ex")
     return out, (lse if want_lse else None), chunk_idx, group_idx
+
+
+def attend_staged_sizes(shape: Shape, group, k_group):
+    pages, nbytes = ctypes.c_int64(), ctypes.c_size_t()
+    _check(_lib.hga_attend_staged_sizes(ctypes.byref(shape), group, k_group, ctypes.byref(pages),
+                                        ctypes.byref(nbytes)), "hga_attend_staged_sizes")
+    return pages.value, nbytes.value
+
+
+def attend_staged(Q, K, V, group_idx, group, scale=0.0, want_lse=True, out=None, lse=None,
+                  pools=None, workspace=None):
+    """attend for slowly read K/V (e.g. pinned host memory): each (sequence, KV
+    head)'s distinct routed groups are copied once into a device pool, then
+    attention reads the pool. Same results as attend."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    _need(V, "V", 4, host_ok=True)
+    _need(group_idx, "group_idx", 4)
+    B, Hq, Nq, D = Q.shape
+    Bk, Hkv, T, Dk = K.shape
+    if (Bk, Dk) != (B, D) or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K/V do not match Q")
+    k_group = group_idx.shape[3]
+    shape = _shape(Q, Hkv, T)
+    pages, nbytes = attend_staged_sizes(shape, group, k_group)
+    ws = workspace if workspace is not None else _workspace(Q.device, "staged", nbytes)
+    if pools is None:
+        kp = _workspace(Q.device, "pool_k", pages * group * D * Q.element_size())
+        vp = _workspace(Q.device, "pool_v", pages * group * D * Q.element_size())
+    else:
+        kp, vp = pools
+    if out is None:
+        out = torch.empty_like(Q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    _check(_lib.hga_attend_staged(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q),
+                                  _ptr(group_idx), k_group, group, float(scale), _ptr(out),
+                                  _ptr(lse if want_lse else None), _ptr(kp), _ptr(vp), pages,
+                                  _ptr(ws), ws.numel(), _stream(Q.device)), "hga_attend_staged")
+    return out, (lse if want_lse else None)
+

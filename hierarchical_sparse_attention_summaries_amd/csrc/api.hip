@@ -438,6 +438,99 @@ int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_
   return HGA_OK;
 }
 
+// Workspace of hga_attend_staged: the attention's (counters first), then the
+// staging tables.
+struct StagedWorkspace {
+  hga::StagePlan stage;
+  hga::AttendPlan attend;
+  size_t marks, table, pages, counts, bytes;
+};
+StagedWorkspace staged_workspace(const hga_shape* s, int32_t group, int32_t k_group) {
+  StagedWorkspace w{};
+  w.stage = hga::plan_stage(s->batch, s->q_heads, s->kv_heads, s->n_queries, s->seq_len, group,
+                            k_group);
+  const int64_t rows = s->batch * s->q_heads * s->n_queries;
+  w.attend = hga::plan_attend(rows, s->head_dim, group, k_group);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  w.marks = up(w.attend.bytes);
+  w.table = up(w.marks + static_cast<size_t>(w.stage.units * w.stage.words) * 4);
+  w.pages = up(w.table + static_cast<size_t>(w.stage.units * w.stage.n_g) * 4);
+  w.counts = up(w.pages + static_cast<size_t>(w.stage.units * w.stage.cap) * 4);
+  w.bytes = up(w.counts + static_cast<size_t>(w.stage.units) * 4);
+  return w;
+}
+
+int hga_attend_staged_sizes(const hga_shape* shape, int32_t group, int32_t k_group,
+                            int64_t* pool_pages, size_t* workspace_bytes) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!pool_pages || !workspace_bytes) return HGA_ERR_NULL;
+  if (group < 1 || group > 65536 || k_group < 1) return HGA_ERR_PARAM;
+  const StagedWorkspace w = staged_workspace(shape, group, k_group);
+  if (w.stage.pool_pages >= kMaxDim) return HGA_ERR_SHAPE;
+  *pool_pages = w.stage.pool_pages;
+  *workspace_bytes = w.bytes;
+  return HGA_OK;
+}
+
+int hga_attend_staged(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                      int32_t dtype, const int32_t* group_idx, int32_t k_group, int32_t group,
+                      float scale, void* O, float* lse, void* K_pool, void* V_pool,
+                      int64_t pool_pages, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !group_idx || !O || !K_pool || !V_pool || !workspace) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  if (group < 1 || group > 65536 || k_group < 1) return HGA_ERR_PARAM;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(K_pool) ||
+      !aligned16(V_pool) || !aligned16(workspace))
+    return HGA_ERR_LAYOUT;
+  const StagedWorkspace w = staged_workspace(shape, group, k_group);
+  if (w.stage.pool_pages >= kMaxDim) return HGA_ERR_SHAPE;
+  if (pool_pages < w.stage.pool_pages) return HGA_ERR_PARAM;
+  if (workspace_bytes < w.bytes) return HGA_ERR_WORKSPACE;
+  const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
+  if (rows * w.attend.n_splits >= kMaxDim) return HGA_ERR_SHAPE;
+  char* ws = static_cast<char*>(workspace);
+  hga::StageArgs sa{};
+  sa.K = K;
+  sa.V = V;
+  sa.K_pool = K_pool;
+  sa.V_pool = V_pool;
+  sa.group_idx = group_idx;
+  sa.B = shape->batch;
+  sa.Hq = static_cast<int>(shape->q_heads);
+  sa.Hkv = static_cast<int>(shape->kv_heads);
+  sa.Nq = static_cast<int>(shape->n_queries);
+  sa.T = shape->seq_len;
+  sa.D = static_cast<int>(shape->head_dim);
+  sa.G = group;
+  sa.k_g = k_group;
+  sa.marks = reinterpret_cast<uint32_t*>(ws + w.marks);
+  sa.block_table = reinterpret_cast<int32_t*>(ws + w.table);
+  sa.page_group = reinterpret_cast<int32_t*>(ws + w.pages);
+  sa.counts = reinterpret_cast<int32_t*>(ws + w.counts);
+  sa.plan = w.stage;
+  hipError_t e = hga::launch_stage(sa, dtype, as_stream(stream));
+  if (e != hipSuccess) return HGA_ERR_HIP;
+  // attention over the pool: B*Hkv sequences of one KV head and r query heads
+  // each (the same memory order as [B, Hq, ...]), pages of one group
+  const int64_t r = shape->q_heads / shape->kv_heads;
+  const hga_shape s2{shape->batch * shape->kv_heads, r, 1, shape->n_queries, shape->seq_len,
+                     shape->head_dim};
+  hga::KvLayout L{};
+  L.paged = 1;
+  L.page_tokens = group;
+  L.max_pages = static_cast<int>(w.stage.n_g);
+  L.n_pages = static_cast<int>(pool_pages);
+  L.block_table = sa.block_table;
+  const hga::AttendArgs aa = attend_args(&s2, L, Q, K_pool, V_pool, group_idx, k_group, group,
+                                         scale, O, lse, workspace, w.attend);
+  e = hga::launch_attend(aa, dtype, w.attend, as_stream(stream));
+  return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
+}
+
 int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
                                int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one) {
   int st = check_shape(shape);

@@ -150,6 +150,32 @@ bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int6
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
                               int dtype, unsigned* ready, hipStream_t stream);
 
+// Host-memory tier: the routed groups of each (sequence, KV head), over all
+// its query rows, copied once into a device pool of [pool_pages, G, D] pages;
+// unit = sequence * Hkv + KV head owns pool pages [unit * cap, unit * cap +
+// count[unit]) in ascending group order.
+struct StagePlan {
+  int64_t n_g, units, cap, words, pool_pages;
+};
+StagePlan plan_stage(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int G, int k_g);
+struct StageArgs {
+  const void* K;
+  const void* V;
+  void* K_pool;
+  void* V_pool;
+  const int32_t* group_idx;
+  int64_t B;
+  int Hq, Hkv, Nq;
+  int64_t T;
+  int D, G, k_g;
+  uint32_t* marks;       // workspace [units, words]
+  int32_t* block_table;  // workspace [units, n_g]: pool page of each group, or -1
+  int32_t* page_group;   // workspace [units, cap]: group of each page
+  int32_t* counts;       // workspace [units]: pages used
+  StagePlan plan;
+};
+hipError_t launch_stage(const StageArgs& a, int dtype, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace hga

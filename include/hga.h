@@ -220,8 +220,9 @@ int hga_route_ex(const hga_shape* shape, const hga_kv_layout* layout, const void
 /* Decode-step form of step 1 + step 2: hga_update_summaries_ex(newest = Nq)
  * followed by hga_route_ex, with the same results bit for bit. For small
  * batches (B*Hq*Nq <= 1024, Nq <= chunk, chunk/group <= 16, the routing
- * state within 64 KiB of LDS, not the MFMA prefill case) it runs as one launch: each routing workgroup recomputes the
- * newest chunks of its sequence from K, writes them to chunk_mean/group_mean
+ * state within 64 KiB of LDS, not the MFMA prefill case) it runs as one
+ * launch: each routing workgroup recomputes the newest chunks of its sequence
+ * from K, writes them to chunk_mean/group_mean
  * and scores with them; otherwise it enqueues the two calls. K is the cache the
  * layout describes. Workspace as hga_route_workspace_size. */
 int hga_route_fresh_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
@@ -237,6 +238,33 @@ int hga_attend_ex(const hga_shape* shape, const hga_kv_layout* layout, const voi
                   const void* K, const void* V, int32_t dtype, const int32_t* group_idx,
                   int32_t k_group, int32_t group, float scale, void* O, float* lse,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pool pages and workspace bytes hga_attend_staged needs for this shape. */
+int hga_attend_staged_sizes(const hga_shape* shape, int32_t group, int32_t k_group,
+                            int64_t* pool_pages, size_t* workspace_bytes);
+
+/*
+ * Step 3 for K/V in memory the device reads slowly, such as pinned host memory
+ * (HGA abstract: the full K/V need not sit in device memory; only the routed
+ * tokens are fetched). The r*Nq query rows of one (sequence, KV head) share
+ * much of their routing, so the routed groups are first deduplicated per
+ * (sequence, KV head) and each is copied once into a device pool; attention
+ * then reads the pool. O and lse equal hga_attend's on the same arguments,
+ * bit for bit.
+ *   Q, K, V, group_idx, O, lse, scale: as hga_attend (K, V dense
+ *             [B, Hkv, T, D], in any memory the device can address).
+ *   K_pool, V_pool: device memory of pool_pages pages of [group, D] elements
+ *             of `dtype` each, pool_pages >= the count hga_attend_staged_sizes
+ *             gives (B*Hkv*min(ceil(T/group), r*Nq*k_group)); scratch.
+ *   workspace: hga_attend_staged_sizes bytes; first 64 KiB zero, as always.
+ * The bytes read from K and V are the distinct routed groups' (what
+ * crosses the host link), not every row's.
+ */
+int hga_attend_staged(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                      int32_t dtype, const int32_t* group_idx, int32_t k_group, int32_t group,
+                      float scale, void* O, float* lse, void* K_pool, void* V_pool,
+                      int64_t pool_pages, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Workspace bytes hga_decode_step_ex needs. As for every call here, the
  * workspace's first 64 KiB must be zero before its first use and are left

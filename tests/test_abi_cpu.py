@@ -182,3 +182,29 @@ def test_decode_step_rejects_before_launch():
     assert d(ctypes.byref(s), *bad) == LAYOUT
     assert d(ctypes.byref(_shape(head_dim=96)), *args) == SHAPE
     assert d(None, *args) == NULL
+
+
+def test_attend_staged_rejects_before_launch():
+    L = hga.lib()
+    pages, n = ctypes.c_int64(), ctypes.c_size_t()
+    s = _shape(batch=4, seq_len=262144)
+    assert L.hga_attend_staged_sizes(ctypes.byref(s), 32, 256, ctypes.byref(pages), ctypes.byref(n)) == OK
+    # per (sequence, KV head): min(ceil(T/G), r*Nq*k_g) pages
+    assert pages.value == 4 * 4 * min(262144 // 32, 8 * 1 * 256)
+    f = L.hga_attend_staged
+    # shape, Q, K, V, dtype, group_idx, k_group, group, scale, O, lse, K_pool, V_pool, pages, ws, bytes, stream
+    args = [FAKE, FAKE, FAKE, 1, FAKE, 256, 32, 0.0, FAKE, None, FAKE, FAKE, pages.value, FAKE,
+            n.value, None]
+    for i in (0, 1, 2, 4, 8, 10, 11, 13):
+        bad = list(args); bad[i] = None
+        assert f(ctypes.byref(s), *bad) == NULL, i
+    bad = list(args); bad[3] = 4
+    assert f(ctypes.byref(s), *bad) == DTYPE
+    bad = list(args); bad[12] = pages.value - 1
+    assert f(ctypes.byref(s), *bad) == PARAM
+    bad = list(args); bad[14] = n.value - 1
+    assert f(ctypes.byref(s), *bad) == WORKSPACE
+    bad = list(args); bad[10] = MIS
+    assert f(ctypes.byref(s), *bad) == LAYOUT
+    bad = list(args); bad[5] = 0
+    assert f(ctypes.byref(s), *bad) == PARAM

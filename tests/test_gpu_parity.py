@@ -543,3 +543,48 @@ def test_prefill_ragged_with_queries_before_the_first_key():
               cidx=out["cidx"][2:3, :, short:], gidx=out["gidx"][2:3, :, short:],
               O=out["O"][2:3, :, short:], lse=out["lse"][2:3, :, short:])
     check_workload(wb, sub, ob)
+
+
+@pytest.mark.parametrize("case", ["device-bf16", "pinned-bf16-overlap", "pinned-f32-padding"])
+def test_attend_staged_equals_attend(case):
+    """Staged attention (each (sequence, KV head)'s distinct routed groups
+    copied once into a device pool) gives attend's results bit for bit, with
+    device or pinned host K/V, overlapping routes across the heads of a KV
+    head, and -1 padding."""
+    log(f"case attend-staged-{case}")
+    if case == "device-bf16":
+        w = DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2)
+    elif case == "pinned-bf16-overlap":       # many groups per row: heads overlap
+        w = DECODE_64K.with_(B=3, Hq=16, Hkv=2, T=4096, Nq=3, k_chunk=12, k_group=96, plants=0)
+    else:
+        w = Workload("staged-f32", 2, 4, 2, 64, 1000, 5, 64, 16, 2, 20, 1e4, "f32", 0)
+    inp = generate(w)
+    out = run_hip(w, inp)
+    K, V = out["K"], out["V"]
+    if case != "device-bf16":
+        from tests.gpu_runner import to_pinned
+        K, V = to_pinned(inp.K, w.dtype), to_pinned(inp.V, w.dtype)
+    O_d, lse_d = hga.attend(out["Q"], K, V, out["gidx"], w.group)
+    O_s, lse_s = hga.attend_staged(out["Q"], K, V, out["gidx"], w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(O_s, O_d) and torch.equal(lse_s, lse_d)
+    assert torch.equal(O_s, out["O"])
+    if case == "pinned-f32-padding":         # the routing pads with -1 here
+        assert (out["gidx"] == -1).any()
+
+
+def test_attend_staged_host_tier_b4_t262144():
+    """The host-memory tier workload through staged attention equals the
+    direct reads of pinned host K/V, and moves about half the bytes."""
+    w = HOST_TIER
+    log(f"case attend-staged-{w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)          # direct: every row reads its groups from host memory
+    O_s, lse_s = hga.attend_staged(out["Q"], out["K"], out["V"], out["gidx"], w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(O_s, out["O"]) and torch.equal(lse_s, out["lse"])
+    g = out["gidx"].cpu().numpy()
+    r = w.Hq // w.Hkv
+    distinct = sum(len(np.unique(g[b, kv * r:(kv + 1) * r][g[b, kv * r:(kv + 1) * r] >= 0]))
+                   for b in range(w.B) for kv in range(w.Hkv))
+    assert distinct < 0.75 * int((g >= 0).sum())
