@@ -76,6 +76,7 @@ KERNEL_SOURCES = {
     "attend": ["attend.hip", "hga_attend_body.h", "hga_device.h", "hga_internal.h"],
     "decode_step": ["decode.hip", "hga_attend_body.h", "hga_route_row_body.h", "hga_device.h",
                     "hga_internal.h", "hga_select.h", "hga_summary.h"],
+    "summaries": ["summaries.hip", "hga_summary.h", "hga_device.h", "hga_internal.h"],
 }
 
 
@@ -137,7 +138,8 @@ def main():
         p_args.steps, p_args.warmup = 5, 2
         pf = measure(ALL[PREFILL], p_args, primary=False)
         out["prefill"] = {k: pf[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
-                                             "kernels_us", "roofline", "roofline_step", "mfma")}
+                                             "kernels_us", "roofline", "roofline_step",
+                                             "roofline_build", "mfma")}
     if not args.no_sweep:
         # the batch-16 context sweep; its 64K point is the secondary run below
         from synth import SWEEP
@@ -163,8 +165,8 @@ def main():
             sec = measure(w2, sec_args, primary=False)
             out["secondary"] = {k: sec[k] for k in ("config", "value", "unit", "ms_per_step",
                                                     "steps", "hbm_gbs_step", "roofline",
-                                                    "roofline_step", "kernels_us",
-                                                    "latency_us")}
+                                                    "roofline_step", "roofline_build",
+                                                    "kernels_us", "latency_us")}
     print(json.dumps(out))
 
 
@@ -263,6 +265,11 @@ def measure(w, args, primary: bool):
     gidx = torch.empty_like(gidx0)
     O = torch.empty_like(Q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+
+    def k_build(s):
+        # step 1 in full (once per prefill; not part of a decode step)
+        K, V, cm, gm = sets[s]
+        hga.build_summaries(K, w.chunk, w.group, cm, gm)
 
     def k_update(s):
         K, V, cm, gm = sets[s]
@@ -410,6 +417,9 @@ def measure(w, args, primary: bool):
     n_k = max(50, min(args.steps, 400))
     names = ["decode_step", "route_fresh", "attend", "update", "route"]   # the step is the first
     fns = [k_decode, k_route_fresh, k_attend, k_update, k_route]
+    if not w.host_kv:   # a full build from host memory would take the link for seconds
+        names.append("build")
+        fns.append(k_build)
     if w.host_kv:
         names.append("attend_staged")
         fns.append(k_attend_staged)
@@ -463,6 +473,10 @@ def measure(w, args, primary: bool):
     roofline["gathered_gbs"] = round(gather_bytes / (attend_us * 1e-6) / 1e9, 1)
     roofline_step = roof("decode_step", step_bytes, decode_us)
     roofline_step["launches"] = 1 if decode_one_launch else 2
+    # step 1 in full: every key read once, every summary written once
+    build_bytes = K0.numel() * esize + w.B * w.Hkv * (w.n_chunks + w.n_groups) * w.D * 4
+    roofline_build = (roof("summaries", build_bytes, kern_us["build"]["avg"])
+                      if "build" in kern_us else None)
 
     # Many queries per KV head (prefill): scoring is a dense MFMA contraction.
     mfma = None
@@ -509,6 +523,7 @@ def measure(w, args, primary: bool):
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,
         "roofline_step": roofline_step,
+        "roofline_build": roofline_build,
         "kernels_us": {k: round(v["avg"], 3) for k, v in kern_us.items()},
         "latency_us": {"p50": round(pct(lat, 0.5), 2), "p95": round(pct(lat, 0.95), 2),
                        "p99": round(pct(lat, 0.99), 2)},
