@@ -132,7 +132,6 @@ def main():
         ht = measure(ALL[HOST_TIER], h_args, primary=False)
         out["host_tier"] = {k: ht[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
                                                "kernels_us", "host_tier")}
-        out["host_tier"]["step"] = "route_fresh_ex + attend_staged (distinct routed groups staged once)"
     if not args.no_prefill and w.name != PREFILL:
         p_args = argparse.Namespace(**vars(args))
         p_args.steps, p_args.warmup = 5, 2
@@ -518,7 +517,10 @@ def measure(w, args, primary: bool):
                    "k_chunk": w.k_chunk, "k_group": w.k_group,
                    "routed_fraction": round(routed_tokens / (rows * w.T), 5),
                    "cold_cache_copies": S, "hip_graph": use_graph,
-                   "step": "decode_step_ex (newest-keys summary refresh + routing + attention)"},
+                   "step": ("route_fresh_ex + attend_staged (newest-keys summary refresh + "
+                            "routing, then attention over the distinct routed groups staged once)"
+                            if w.host_kv else
+                            "decode_step_ex (newest-keys summary refresh + routing + attention)")},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": step_bytes,
         "roofline": roofline,
