@@ -3,7 +3,8 @@
 // 2606.30709): the first chunk and the query's own chunk are always kept, plus
 // the k_chunk best of the chunks between them; then the k_group best of all
 // groups of the kept chunks that start at or before the query. Used by the
-// fused decode route kernel and by the prefill select kernel.
+// multi-workgroup route (route.hip) and by the select kernel of the
+// three-kernel prefill form (route_prefill.hip).
 #pragma once
 
 #include "hga_device.h"

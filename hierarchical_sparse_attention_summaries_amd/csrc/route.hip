@@ -8,7 +8,7 @@
 // row of the block (the r query heads that share the KV head read the same
 // summary bytes once). The slices' scores go to the workspace; the last
 // workgroup of the block to finish (an atomic arrival count, nobody waits)
-// runs the selection: one wave per query row does a bitwise radix top-k of the
+// runs the selection: one wave per query row does a bitwise radix top-k (two bits per step) of the
 // chunks with ballots, then lists the kept chunks' groups and runs the same
 // top-k on them.
 //
