@@ -8,9 +8,9 @@
 // row of the block (the r query heads that share the KV head read the same
 // summary bytes once). The slices' scores go to the workspace; the last
 // workgroup of the block to finish (an atomic arrival count, nobody waits)
-// runs the selection: one wave per query row does a bitwise radix top-k (two bits per step) of the
-// chunks with ballots, then lists the kept chunks' groups and runs the same
-// top-k on them.
+// runs the selection: one wave per query row does a radix top-k of the chunks
+// with ballots (two bits per step), then lists the kept chunks' groups and
+// runs the same top-k on them.
 //
 // Why all groups are scored: with GQA the r query heads of a KV head each
 // examine (k_chunk + 2) * chunk/group candidate groups; at the budgets used with
