@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["decode", "attend", "route", "route_fresh", "update", "step",
-                                       "copy"])
+                                       "build", "copy"])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the batch-16 64K-context point of the context sweep")
     ap.add_argument("--no-host-tier", action="store_true",
@@ -74,8 +74,9 @@ def kernel_source_hash(names):
 # only while they hash as they did when it was taken.
 KERNEL_SOURCES = {
     "attend": ["attend.hip", "hga_attend_body.h", "hga_device.h", "hga_internal.h"],
-    "decode_step": ["decode.hip", "hga_attend_body.h", "hga_route_row_body.h", "hga_device.h",
-                    "hga_internal.h", "hga_select.h", "hga_summary.h"],
+    "decode_step": ["decode.hip", "hga_attend_body.h", "hga_route_row_launch.h",
+                    "hga_route_row_body.h", "hga_device.h", "hga_internal.h", "hga_select.h",
+                    "hga_summary.h"],
     "summaries": ["summaries.hip", "hga_summary.h", "hga_device.h", "hga_internal.h"],
 }
 
@@ -320,7 +321,7 @@ def measure(w, args, primary: bool):
 
     if args.only:
         fn = {"attend": k_attend, "route": k_route, "update": k_update, "step": step,
-              "route_fresh": k_route_fresh, "decode": k_decode}[args.only]
+              "route_fresh": k_route_fresh, "decode": k_decode, "build": k_build}[args.only]
         k_route(0)
         for k in range(args.warmup + args.steps):
             fn(k % S)
