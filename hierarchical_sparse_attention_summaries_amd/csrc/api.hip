@@ -131,27 +131,30 @@ hga::AttendArgs attend_args(const hga_shape* shape, const hga::KvLayout& L, cons
   return a;
 }
 
-// Whether hga_route_fresh_ex refreshes inside the row route (one launch), and
-// hga_decode_step_ex runs as one launch.
-// `decode`: inside the one-launch decode step (attention's LDS beside it).
+// Whether hga_route_fresh_ex refreshes inside the row route (one launch).
 bool row_fresh_fused(const hga_shape* s, int32_t dtype, int32_t chunk, int32_t group,
-                     int32_t k_chunk, int32_t k_group, bool decode) {
-  if (decode && !hga::decode_step_one_launch(s->batch, s->q_heads, s->kv_heads, s->n_queries,
-                                             s->head_dim, group, k_group))
-    return false;
+                     int32_t k_chunk, int32_t k_group) {
   return hga::use_row_route(s->batch, s->q_heads, s->n_queries, s->seq_len, s->head_dim, chunk,
-                            group, k_chunk, k_group, true,
-                            decode ? hga::decode_step_lds(s->head_dim) : 0) &&
+                            group, k_chunk, k_group, true) &&
          !(dtype == HGA_BF16 &&
            hga::use_prefill_route(dtype, s->q_heads, s->kv_heads, s->n_queries, s->head_dim));
 }
 
-// Workspace of hga_decode_step_ex. The two-call form runs routing and then
-// attention in stream order over the same workspace; the one-launch form keeps
-// its ready flags at counter words [0, rows) and the attention's arrival
-// counters at words [kDecodeAttendCounters, +rows) (rows <= 1024 there), and
-// the attention partials after the counters, as every plan does.
+// Counter words of the one-launch decode step: the attention's split counters
+// sit at [kDecodeAttendCounters, +rows) (rows <= the CU count there), clear of
+// the per-unit scoring counters below them.
 constexpr int kDecodeAttendCounters = 8192;
+
+// Whether hga_decode_step_ex runs as one launch (small batches).
+bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
+                       int32_t k_group) {
+  return hga::decode_step_one_launch(s->batch, s->q_heads, s->kv_heads, s->n_queries, s->seq_len,
+                                     s->head_dim, chunk, group, k_chunk, k_group);
+}
+
+// Workspace of hga_decode_step_ex: the larger of the two-call form (routing,
+// then attention in stream order over the same workspace) and the one-launch
+// form (the attention's counters and partials, then every row's scores).
 size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
                               int32_t k_group) {
   const int64_t rows = s->batch * s->q_heads * s->n_queries;
@@ -159,7 +162,8 @@ size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, 
                                    chunk, group, k_chunk, k_group)
                        .bytes,
                    hga::plan_attend(rows, s->head_dim, group, k_group).bytes,
-                   hga::plan_decode_attend(rows, s->head_dim, k_group).bytes});
+                   hga::decode_step_bytes(s->batch, s->q_heads, s->n_queries, s->seq_len,
+                                          s->head_dim, chunk, group, k_group)});
 }
 
 // Checks a caller's K/V layout against the capacity T and group size and
@@ -332,7 +336,7 @@ int hga_route_fresh_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   hga::KvLayout L;
   st = to_layout(layout, shape->seq_len, group, &L);
   if (st != HGA_OK) return st;
-  if (!row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, false)) {
+  if (!row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group)) {
     // two launches: refresh, then route
     st = summaries_common(K, dtype, layout, shape->batch, shape->kv_heads, shape->seq_len,
                           shape->head_dim, chunk, group, 0, 0, shape->n_queries, chunk_mean,
@@ -539,7 +543,7 @@ int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t ch
   if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
   st = check_route_params(shape, chunk, group, k_chunk, k_group);
   if (st != HGA_OK) return st;
-  *one = row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, true) ? 1 : 0;
+  *one = decode_one_launch(shape, chunk, group, k_chunk, k_group) ? 1 : 0;
   return HGA_OK;
 }
 
@@ -565,7 +569,7 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   if (workspace_bytes < decode_workspace_bytes(shape, chunk, group, k_chunk, k_group))
     return HGA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  if (!row_fresh_fused(shape, dtype, chunk, group, k_chunk, k_group, true)) {
+  if (!decode_one_launch(shape, chunk, group, k_chunk, k_group)) {
     // refresh + route, then attend
     st = hga_route_fresh_ex(shape, layout, Q, K, dtype, chunk_mean, group_mean, chunk, group,
                             k_chunk, k_group, scale, chunk_idx, group_idx, ws, workspace_bytes,
@@ -586,8 +590,7 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   hga::AttendArgs aa = attend_args(shape, L, Q, K, V, group_idx, k_group, group, scale, O, lse,
                                    ws, aplan);
   aa.counters = reinterpret_cast<unsigned*>(ws) + kDecodeAttendCounters;
-  unsigned* ready = reinterpret_cast<unsigned*>(ws);  // the row route itself uses no counters
-  const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ready, as_stream(stream));
+  const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ws, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 

@@ -47,10 +47,14 @@ __device__ __forceinline__ bool wait_ready(const unsigned* flag, bool* s_ok) {
 // `bid % n_splits`. With `ready` set (routing and attention in one launch), it
 // first waits until the row's routing workgroup has published the row's group
 // ids (bounded wait), reads them coherently, and the row's last workgroup
-// clears the flag again.
-template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves>
-__device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_wave, int n_splits,
-                                            int row_base, int bid, unsigned* ready) {
+// clears the flag again. With LDS_IDS the row's group ids are already in LDS
+// (s_ids, k_group entries), chosen by this workgroup itself; `poisoned` then
+// marks a row whose routing could not be completed (its outputs become NaN).
+// Returns true in the workgroup that wrote the row's outputs (its last split).
+template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves, bool LDS_IDS = false>
+__device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_wave, int n_splits,
+                                            int row_base, int bid, unsigned* ready,
+                                            const int* s_ids = nullptr, bool poisoned = false) {
   constexpr int kBodyThreads = WAVES * kWave;
   constexpr int EPL = Elem<TKV>::kPer16;
   constexpr int LPR = D / EPL;        // lanes per token row
@@ -96,7 +100,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
   const int32_t* gl = a.group_idx + static_cast<size_t>(row) * a.k_g;
-  bool timed_out = false;
+  bool timed_out = poisoned;
   if constexpr (WAIT) timed_out = !wait_ready(ready + row, &s_flag);
   const int e0 = (split * WAVES + wave) * groups_per_wave;
   const int e1 = min(e0 + groups_per_wave, a.k_g);
@@ -111,7 +115,9 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
       gb += kWave;
       const int j = gb + lane_id();
       if (j < e1) {
-        if constexpr (WAIT) {
+        if constexpr (LDS_IDS) {
+          g_lane = s_ids[j];
+        } else if constexpr (WAIT) {
           g_lane = load_shared_i32(gl + j);
         } else {
           g_lane = gl[j];
@@ -244,20 +250,18 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
     }
   }
   // A split that gave up waiting poisons its row (NaN survives the merge).
-  if constexpr (WAIT) {
-    if (timed_out) Lsum = __builtin_nanf("");
-  }
+  if (timed_out) Lsum = __builtin_nanf("");
 
   auto finish = [&](float Mx, float Lx, float ox) {
+    // the row is done: clear its flag for the next call (never on a timeout,
+    // whose outputs are NaN)
     if constexpr (WAIT) {
-      // the row is done: clear its flag for the next call (never on a timeout,
-      // whose outputs are NaN)
       if (d == 0 && !timed_out) __hip_atomic_store(ready + row, 0u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-      if (timed_out) {
-        Lx = 1.f;
-        ox = __builtin_nanf("");
-      }
+    }
+    if (timed_out) {
+      Lx = 1.f;
+      ox = __builtin_nanf("");
     }
     if (d < D) {
       const float v = Lx > 0.f ? ox / Lx : 0.f;
@@ -273,7 +277,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
 
   if (n_splits == 1) {
     finish(M, Lsum, acc);
-    return;
+    return true;
   }
   float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
   if (d < D) store_shared(part + 2 + d, acc);
@@ -282,7 +286,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
     store_shared(part + 1, Lsum);
   }
   if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
-    return;
+    return false;
 
   // Pull every split's (m, l, o) into LDS with all loads in flight at once.
   const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
@@ -312,6 +316,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int groups_per_
     }
   }
   finish(Mx, Lx, ox);
+  return true;
 }
 
 

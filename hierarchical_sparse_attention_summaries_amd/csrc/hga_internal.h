@@ -134,21 +134,23 @@ struct AttendArgs {
 hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
                          hipStream_t stream);
 
-// Decode step (refresh + route + attend) as one launch: routing workgroups
-// first, attention workgroups after them waiting on per-row ready flags.
-// Applies where the row route refreshes by itself with the attention's static
-// LDS (decode_step_lds) beside it, not in the prefill case; `ready` holds one
-// zero word per query row and is left zero.
-size_t decode_step_lds(int64_t D);
+// Decode step (refresh + score + select + attend) as one launch, every
+// workgroup resident at once (at most one per CU): each scores a slice of one
+// (sequence, KV head)'s summaries for all its query rows, then selects and
+// attends for one (row, split). The workspace holds the attention plan's
+// counters and partials (plan.bytes), then the scores [rows, n_c + n_g].
 // Attention plan inside the one-launch decode step (8 waves per workgroup).
 AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g);
-// Whether every workgroup of the one-launch decode step is resident at once,
-// one per CU (small batches): routing never queues behind waiting attention,
-// and the big routing form applies.
-bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D, int G,
-                            int k_g);
+// Whether the one-launch form applies: the grid fits one workgroup per CU,
+// the refresh touches at most two chunks of at most 16 groups, and the row's
+// scores and selection fit the LDS.
+bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int64_t D,
+                            int C, int G, int k_c, int k_g);
+// Workspace bytes of the one-launch form.
+size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t T, int64_t D, int C, int G,
+                         int k_g);
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
-                              int dtype, unsigned* ready, hipStream_t stream);
+                              int dtype, void* workspace, hipStream_t stream);
 
 // Host-memory tier: the routed groups of each (sequence, KV head), over all
 // its query rows, copied once into a device pool of [pool_pages, G, D] pages;
