@@ -108,9 +108,10 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
           for (int e = 0; e < 8; ++e) q[r][e] = 0.f;
         }
       }
+      // partial dot products over this lane's 8 dims, value k = j * QB + r
+      float part[NB * QB];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int i = base + first + j * kStride;
 #pragma unroll
         for (int r = 0; r < QB; ++r) {
           float d = q[r][0] * v0[j].x;
@@ -121,10 +122,25 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
           d = fmaf(q[r][5], v1[j].y, d);
           d = fmaf(q[r][6], v1[j].z, d);
           d = fmaf(q[r][7], v1[j].w, d);
-          d = group_sum<LPR>(d);
-          if (i < n && qb + r < nq && (lane % LPR) == 0)
-            store_shared(scores + static_cast<size_t>(row0 + qb + r) * NS + col_of(i), d);
+          part[j * QB + r] = d;
         }
+      }
+      // Sum over the row's LPR lanes, scattered: lane t of the row ends with
+      // value t (D = 128: all 16 values) or values t and QB + t (D = 64), each
+      // with group_sum's bits; then every lane stores its own.
+      static_assert(LPR * (LPR == 16 ? 1 : 2) == NB * QB, "values per row group");
+      const int t = lane % LPR;
+#pragma unroll
+      for (int h = 0; h < NB * QB / LPR; ++h) {
+        float c[LPR];
+#pragma unroll
+        for (int k = 0; k < LPR; ++k) c[k] = part[h * LPR + k];
+        const float d = group_sum_scatter<LPR>(c);
+        const int k = h * LPR + t;
+        const int j = k / QB, r = k % QB;
+        const int i = base + first + j * kStride;
+        if (i < n && qb + r < nq)
+          store_shared(scores + static_cast<size_t>(row0 + qb + r) * NS + col_of(i), d);
       }
     }
   }

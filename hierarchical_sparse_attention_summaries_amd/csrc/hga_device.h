@@ -83,18 +83,51 @@ __device__ __forceinline__ float pair_max(float v) {
 }
 
 // Sum over aligned groups of N lanes (N in 1,2,4,8,16,32,64); every lane of a
-// group gets the group's total. Within a 16-lane DPP row the butterfly is
-// quad xor1, quad xor2, half-row mirror, row mirror; then row pairs and
-// half-waves.
+// group gets the group's total. Within a 16-lane DPP row the butterfly runs
+// largest span first: row mirror (lane t with 15 - t), half-row mirror (t with
+// t ^ 7), quad xor2, quad xor1; then row pairs and half-waves.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if constexpr (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  if constexpr (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
   if constexpr (N >= 16) v += dpp<0x140>(v);  // row_mirror
+  if constexpr (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if constexpr (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
   if constexpr (N >= 32) v = pair_sum<16>(v);
   if constexpr (N >= 64) v = pair_sum<32>(v);
   return v;
+}
+
+// N partial sums per lane over aligned groups of N lanes (N in 2,4,8,16):
+// returns, in lane t of a group, the group total of value t % N, with the
+// same additions in the same order as group_sum<N> on that value alone (so
+// the same bits). Each step keeps the half of its values that its lane's bit
+// selects and adds the partner's copy of that half: N - 1 exchanges instead of
+// N * log2(N).
+template <int N>
+__device__ __forceinline__ float group_sum_scatter(const float (&c)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "2..16 lanes");
+  constexpr int H = N / 2;
+  const bool hi = (__lane_id() & H) != 0;
+  float next[H];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = hi ? c[k + H] : c[k];
+    const float send = hi ? c[k] : c[k + H];
+    if constexpr (N == 16) {
+      next[k] = keep + dpp<0x140>(send);  // row_mirror: the partner differs in bit 3
+    } else if constexpr (N == 8) {
+      next[k] = keep + dpp<0x141>(send);  // row_half_mirror: bit 2
+    } else if constexpr (N == 4) {
+      next[k] = keep + dpp<0x4E>(send);   // quad xor2: bit 1
+    } else {
+      next[k] = keep + dpp<0xB1>(send);   // quad xor1: bit 0
+    }
+  }
+  if constexpr (H == 1) {
+    return next[0];
+  } else {
+    return group_sum_scatter<H>(next);
+  }
 }
 
 // Sum/max over lanes that are S, 2S, 4S, ... apart (S a power of two < 64): the
