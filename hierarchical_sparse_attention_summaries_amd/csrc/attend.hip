@@ -64,6 +64,7 @@ AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves) {
 
 hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
                          hipStream_t stream) {
+  if (use_tile_attend(a, dtype)) return launch_attend_tiles(a, stream);
   if (dtype == kF32)
     return a.D == 64 ? launch_t<float, 64>(a, plan, stream) : launch_t<float, 128>(a, plan, stream);
   return a.D == 64 ? launch_t<uint16_t, 64>(a, plan, stream)

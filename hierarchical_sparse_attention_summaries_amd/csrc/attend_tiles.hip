@@ -1,0 +1,343 @@
+// Step 3 of HGA (abstract of "Hierarchical Global Attention (HGA)", arXiv
+// 2606.30709) for many queries per head (chunked prefill): exact attention of
+// a tile of query rows over the union of their routed groups, on MFMA.
+//
+// Neighbouring query rows of one head share many routed groups, so a tile of
+// 128 consecutive rows reads each group of the tile's union once (about a
+// tenth of what per-row gathers read at a 64K context) and runs the products
+// on MFMA 16x16x32 bf16, masking per row: a row takes a group's tokens only if
+// it routed the group, and only up to its own position.
+//
+// Layout, per wave (16 rows): S^T = K . Q^T with K rows as the A operand and
+// the wave's query rows as B, so that each lane ends up with 8 scores of one
+// row (two 16-token blocks of a group); the online softmax keeps (m, l) per row
+// in the 4 lanes that hold it; O^T = V^T . P^T with the staged V^T as A and the
+// lane's own probabilities as B (the 32 tokens of a group in the lane order
+// the scores came in), so each lane accumulates 32 dims of its own row and the
+// rescaling stays lane-local. P enters the product as bf16 hi + lo parts, so
+// the accumulation carries P to about 2^-17 relative.
+#include <math.h>
+
+#include "hga_device.h"
+#include "hga_internal.h"
+
+namespace hga {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTR = 128;                         // query rows per tile (workgroup)
+constexpr int kTW = 8;                           // waves, 16 rows each
+constexpr int kTThreads = kTW * kWave;
+constexpr int kTG = 32;                          // tokens per group
+constexpr int kTD = 128;                         // head dim
+constexpr int kStageTok = 2 * kTG;               // two groups staged per step
+constexpr int kKStride = kTD + 8;                // bf16 per staged K row (padded)
+constexpr int kVStride = kStageTok + 8;          // bf16 per staged V^T row (padded)
+constexpr int kTileMaxGroups = 2048;             // groups of the context (mask rows)
+
+struct TileLds {
+  uint32_t mask[kTileMaxGroups][kTR / 32];       // rows of the tile that routed each group
+  int list[kTileMaxGroups];                      // the union, ascending
+  alignas(16) uint16_t k[kStageTok * kKStride];  // staged K rows
+  alignas(16) uint16_t vt[kTD * kVStride];       // staged V^T
+  int wave_count[kTW];
+  int n_union;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as bf16 (round to nearest even, one conversion
+// instruction), and what those bf16 values leave over, also as bf16: x ~ hi + lo.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float b0 = __uint_as_float(hi << 16), b1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - b0, x1 - b1}, bf16x2));
+}
+
+// Workgroup barrier ordering LDS only: unlike __syncthreads(), it does not
+// wait for this thread's global loads, so loads issued steps ahead stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// V^T is staged with the token index of dim d XORed with vt_swizzle(d) (a
+// multiple of 4, so the 4-token blocks the operands read stay whole): the
+// transposing stores of a wave then spread over the LDS banks.
+__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) * 4; }
+
+// This thread's share of one step (zeros past the union's end, the context's
+// end, or a page out of range): K of token t / 16 of each of the step's two
+// groups, and V of tokens 2j, 2j + 1 (j = (t % 256) / 16) of group t / 256;
+// dims (t % 16) * 8 .. +7 each.
+struct StepRegs {
+  uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s, int n_u, int b,
+                                           int kv, int step, StepRegs& r) {
+  const int t = static_cast<int>(threadIdx.x);
+  const int col = (t % 16) * 8;
+  const uint16_t* K = static_cast<const uint16_t*>(a.K);
+  const uint16_t* V = static_cast<const uint16_t*>(a.V);
+  // the global row of token x of the step's group gi, or -1
+  auto row_of = [&](int gi, int x) -> int64_t {
+    const int u = step * 2 + gi;
+    if (u >= n_u) return -1;
+    const int tok = s.list[u] * kTG + x;
+    return tok < a.T ? kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, tok) : -1;
+  };
+  const int64_t k0 = row_of(0, t / 16), k1 = row_of(1, t / 16);
+  const int vg = t / 256, vx = ((t % 256) / 16) * 2;
+  const int64_t v0 = row_of(vg, vx), v1 = row_of(vg, vx + 1);
+  r.k0 = k0 >= 0 ? ld16(K + k0 + col) : make_uint4(0, 0, 0, 0);
+  r.k1 = k1 >= 0 ? ld16(K + k1 + col) : make_uint4(0, 0, 0, 0);
+  r.v0 = v0 >= 0 ? ld16(V + v0 + col) : make_uint4(0, 0, 0, 0);
+  r.v1 = v1 >= 0 ? ld16(V + v1 + col) : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void stash_step(TileLds& s, const StepRegs& r) {
+  const int t = static_cast<int>(threadIdx.x);
+  const int col = (t % 16) * 8;
+  *reinterpret_cast<uint4*>(&s.k[(t / 16) * kKStride + col]) = r.k0;
+  *reinterpret_cast<uint4*>(&s.k[(kTG + t / 16) * kKStride + col]) = r.k1;
+  // V^T: dims col .. col+7 of tokens x, x + 1 (one 32-bit word each)
+  const int x = (t / 256) * kTG + ((t % 256) / 16) * 2;
+  const uint32_t a0[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w};
+  const uint32_t a1[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+  uint32_t* vt = reinterpret_cast<uint32_t*>(s.vt);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int d = col + 2 * e;
+    vt[(d * kVStride + (x ^ vt_swizzle(d))) / 2] = (a0[e] & 0xffffu) | (a1[e] << 16);
+    vt[((d + 1) * kVStride + (x ^ vt_swizzle(d + 1))) / 2] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+  }
+}
+
+__global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a,
+                                                                     int tiles_per_head) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  __shared__ TileLds s;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int tile = static_cast<int>(blockIdx.x) % tiles_per_head;
+  const int bh = static_cast<int>(blockIdx.x) / tiles_per_head;  // b * Hq + h
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int kv = h / (a.Hq / a.Hkv);
+  const int i0 = tile * kTR;
+  const int nrows = min(kTR, a.Nq - i0);
+  const int Tb = seq_len_of(a.kv, b, a.T);
+  const int n_g = (a.T + kTG - 1) / kTG;
+  const size_t row0 = static_cast<size_t>(bh) * a.Nq + i0;  // global row of tile row 0
+
+  // 1. Which rows of the tile routed which group.
+  for (int k = tid; k < n_g * (kTR / 32); k += kTThreads) (&s.mask[0][0])[k] = 0u;
+  __syncthreads();
+  for (int k = tid; k < nrows * a.k_g; k += kTThreads) {
+    const int r = k / a.k_g;
+    const int g = a.group_idx[(row0 + r) * a.k_g + k % a.k_g];
+    if (g >= 0 && g < n_g) atomicOr(&s.mask[g][r >> 5], 1u << (r & 31));
+  }
+  __syncthreads();
+
+  // 2. The union of the tile's groups, ascending: slot j covers groups
+  // [j * kTThreads, +kTThreads), one per thread.
+  int n_u = 0;
+  for (int base = 0; base < n_g; base += kTThreads) {
+    const int g = base + tid;
+    bool present = false;
+    if (g < n_g) {
+#pragma unroll
+      for (int w = 0; w < kTR / 32; ++w) present = present || s.mask[g][w] != 0u;
+    }
+    const uint64_t m = ballot(present);
+    if (lane == 0) s.wave_count[wave] = __popcll(m);
+    __syncthreads();
+    int before = n_u;
+    for (int w = 0; w < wave; ++w) before += s.wave_count[w];
+    int total = n_u;
+    for (int w = 0; w < kTW; ++w) total += s.wave_count[w];
+    if (present) s.list[before + bits_below(m)] = g;
+    n_u = total;
+    __syncthreads();
+  }
+
+  // 3. This lane's query row (one of the wave's 16) as the B operand.
+  const int a8 = (lane / 16) * 8;          // k offset of this lane's operand slice
+  const int a4 = (lane / 16) * 4;          // token / dim offset of its result slice
+  const int my_r = wave * 16 + lane % 16;  // tile row
+  const bool row_ok = my_r < nrows;
+  const int p_r = Tb - a.Nq + i0 + my_r;   // its position (rows past the tile: unused)
+  uint4 qB[kTD / 32];
+#pragma unroll
+  for (int ks = 0; ks < kTD / 32; ++ks) {
+    qB[ks] = row_ok ? ld16(static_cast<const uint16_t*>(a.Q) + (row0 + my_r) * kTD + ks * 32 + a8)
+                    : make_uint4(0, 0, 0, 0);
+  }
+  const float sl2 = a.scale * kLog2e;
+  const int mword = wave >> 1, mshift = (wave & 1) * 16;
+
+  f32x4 o[kTD / 16];
+#pragma unroll
+  for (int d = 0; d < kTD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  // One step: two groups of the union, staged in LDS.
+  auto compute = [&](int step) {
+    const int u0 = step * 2;
+    const int g0 = s.list[u0];
+    const int g1 = u0 + 1 < n_u ? s.list[u0 + 1] : -1;
+    const uint32_t bits0 = (s.mask[g0][mword] >> mshift) & 0xFFFFu;
+    const uint32_t bits1 = g1 >= 0 ? (s.mask[g1][mword] >> mshift) & 0xFFFFu : 0u;
+    if ((bits0 | bits1) == 0u) return;  // none of the wave's rows takes these groups
+    // S^T: 4 blocks of 16 tokens x the wave's 16 rows
+    f32x4 sacc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kTD / 32; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(
+            &s.k[(tb * 16 + lane % 16) * kKStride + ks * 32 + a8]);
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qB[ks]),
+                                                           sacc[tb], 0, 0, 0);
+      }
+    }
+    // mask (routed group, causal) and scale to base 2: token x of group g is
+    // taken iff the row routed g and x <= p - g * G
+    const int lim0 = (row_ok && ((bits0 >> (lane % 16)) & 1u)) ? p_r - g0 * kTG : -1;
+    const int lim1 = (row_ok && ((bits1 >> (lane % 16)) & 1u)) ? p_r - g1 * kTG : -1;
+    float sv[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int lim = tb < 2 ? lim0 : lim1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[tb][i] = ((tb & 1) * 16 + a4 + i <= lim) ? sacc[tb][i] * sl2 : -INFINITY;
+        mt = fmaxf(mt, sv[tb][i]);
+      }
+    }
+    mt = pair_max<16>(mt);
+    mt = pair_max<32>(mt);
+    const float m_new = fmaxf(m, mt);
+    // rescale only where a row's running maximum moved (rarely, once warm)
+    if (ballot(m_new > m) != 0u) {
+      const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= corr;
+#pragma unroll
+      for (int d = 0; d < kTD / 16; ++d) o[d] *= corr;
+    }
+    m = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // rows with nothing yet: p = 0
+    float p[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[tb][i] = __builtin_amdgcn_exp2f(sv[tb][i] - m_use);
+        l += p[tb][i];
+      }
+    // O^T += V^T . P^T, one group at a time, P as bf16 hi + lo
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      if ((gi == 0 ? bits0 : bits1) == 0u) continue;  // uniform over the wave
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 2 * e;  // operand slots j, j + 1: tokens of block 2gi (j < 4) or 2gi + 1
+        const float x0 = j < 4 ? p[2 * gi][j] : p[2 * gi + 1][j - 4];
+        const float x1 = j < 4 ? p[2 * gi][j + 1] : p[2 * gi + 1][j - 3];
+        split_pair(x0, x1, hw[e], lw[e]);
+      }
+      const bf16x8 ph = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 pl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+      for (int d = 0; d < kTD / 16; ++d) {
+        const int dim = d * 16 + lane % 16;
+        const uint16_t* vrow = &s.vt[dim * kVStride];
+        const int sw = vt_swizzle(dim);
+        const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + a4) ^ sw));
+        const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + 16 + a4) ^ sw));
+        const bf16x8 va = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, o[d], 0, 0, 0);
+      }
+    }
+  };
+
+  // 4. The union in steps of two groups. One workgroup per CU (its LDS), so
+  // each step's loads go out four steps ahead of its use: 128 KiB in flight.
+  const int n_st = (n_u + 1) / 2;
+  StepRegs r0, r1, r2, r3;
+  fetch_step(a, s, n_u, b, kv, 0, r0);
+  fetch_step(a, s, n_u, b, kv, 1, r1);
+  fetch_step(a, s, n_u, b, kv, 2, r2);
+  fetch_step(a, s, n_u, b, kv, 3, r3);
+  auto step = [&](int st, StepRegs& r) {
+    stash_step(s, r);
+    lds_barrier();
+    fetch_step(a, s, n_u, b, kv, st + 4, r);
+    compute(st);
+    lds_barrier();
+  };
+  for (int st = 0; st < n_st; st += 4) {
+    step(st, r0);
+    if (st + 1 >= n_st) break;
+    step(st + 1, r1);
+    if (st + 2 >= n_st) break;
+    step(st + 2, r2);
+    if (st + 3 >= n_st) break;
+    step(st + 3, r3);
+  }
+
+  // 5. The row's total over its 4 lanes; each lane writes its 32 dims.
+  l = pair_sum<16>(l);
+  l = pair_sum<32>(l);
+  if (row_ok) {
+    const size_t orow = (row0 + my_r) * kTD;
+    uint16_t* O = static_cast<uint16_t*>(a.O);
+#pragma unroll
+    for (int d = 0; d < kTD / 16; ++d) {
+      uint32_t w[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float v0 = l > 0.f ? o[d][2 * z] / l : 0.f;
+        const float v1 = l > 0.f ? o[d][2 * z + 1] / l : 0.f;
+        w[z] = bf16_bits(v0) | (bf16_bits(v1) << 16);
+      }
+      *reinterpret_cast<uint2*>(O + orow + d * 16 + a4) = make_uint2(w[0], w[1]);
+    }
+    if (a.lse && lane < 16) a.lse[row0 + my_r] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool use_tile_attend(const AttendArgs& a, int dtype) {
+  return dtype == kBF16 && a.D == kTD && a.G == kTG && (a.T + kTG - 1) / kTG <= kTileMaxGroups &&
+         a.Nq >= kTR;
+}
+
+hipError_t launch_attend_tiles(const AttendArgs& a, hipStream_t stream) {
+  const int tiles_per_head = (a.Nq + kTR - 1) / kTR;
+  const int64_t grid = static_cast<int64_t>(a.B) * a.Hq * tiles_per_head;
+  hipLaunchKernelGGL(attend_tiles_kernel, dim3(static_cast<unsigned>(grid)), dim3(kTThreads), 0,
+                     stream, a, tiles_per_head);
+  return hipGetLastError();
+}
+
+}  // namespace hga

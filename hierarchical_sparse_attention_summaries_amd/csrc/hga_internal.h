@@ -133,6 +133,12 @@ struct AttendArgs {
 };
 hipError_t launch_attend(const AttendArgs& a, int dtype, const AttendPlan& plan,
                          hipStream_t stream);
+// Many query rows per head (chunked prefill; bf16, D 128, G 32, at most 2048
+// groups): tiles of 128 consecutive rows of one head attend over the union of
+// their routed groups on MFMA, each group read once per tile. launch_attend
+// takes this path by itself where it applies.
+bool use_tile_attend(const AttendArgs& a, int dtype);
+hipError_t launch_attend_tiles(const AttendArgs& a, hipStream_t stream);
 
 // Decode step (refresh + score + select + attend) as one launch, every
 // workgroup resident at once (at most one per CU): each scores a slice of one

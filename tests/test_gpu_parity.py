@@ -77,6 +77,16 @@ PREFILL_SMALL = [
 ]
 
 
+# Query rows in tiles of 128 per head (bf16, D 128, G 32): the prefill
+# attention runs on MFMA over each tile's union of routed groups. Full tiles
+# and a partial last tile; one tile exactly, with B = 2 and one query head per
+# KV head.
+PREFILL_TILES = [
+    Workload("prefill-tiles-nq300", 1, 8, 2, 128, 4096, 300, 128, 32, 4, 8, 1e6, "bf16", 2),
+    Workload("prefill-tiles-b2-mha", 2, 2, 2, 128, 2048, 128, 64, 32, 5, 6, 1e4, "bf16", 0),
+]
+
+
 # More than 1024 query rows without the MFMA path: the multi-workgroup route
 # (dense scoring of a KV head's summaries, last-arriving workgroup selects).
 FUSED_ROUTE = [
@@ -95,6 +105,14 @@ def test_fused_route_many_rows(w):
 
 @pytest.mark.parametrize("w", PREFILL_SMALL, ids=lambda w: w.name)
 def test_prefill_small(w):
+    log(f"case {w.name}")
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+
+
+@pytest.mark.parametrize("w", PREFILL_TILES, ids=lambda w: w.name)
+def test_prefill_tiles(w):
     log(f"case {w.name}")
     inp = generate(w)
     out = run_hip(w, inp)
@@ -536,6 +554,38 @@ def test_prefill_ragged_with_queries_before_the_first_key():
     check_ragged(w.with_(B=2), inp, seq_lens[:2], {k: v[:2] for k, v in out.items()})
     Tb, short = seq_lens[2], w.Nq - seq_lens[2]          # queries 0..short-1 sit before key 0
     assert (out["gidx"][2, :, :short] == -1).all() and (out["cidx"][2, :, :short] == -1).all()
+    assert (out["O"][2, :, :short] == 0).all() and torch.isinf(out["lse"][2, :, :short]).all()
+    wb = w.with_(B=1, T=Tb, Nq=Tb)
+    sub = Inputs(wb, inp.seed, inp.Q[2:3, :, short:], inp.K[2:3, :, :Tb], inp.V[2:3, :, :Tb])
+    ob = dict(cm=out["cm"][2:3, :, :wb.n_chunks], gm=out["gm"][2:3, :, :wb.n_groups],
+              cidx=out["cidx"][2:3, :, short:], gidx=out["gidx"][2:3, :, short:],
+              O=out["O"][2:3, :, short:], lse=out["lse"][2:3, :, short:])
+    check_workload(wb, sub, ob)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["dense", "paged"])
+def test_prefill_tiles_ragged(paged):
+    """Tile attention (128-row tiles over the union of routed groups) on a
+    ragged batch, dense or paged: the shortest sequence holds fewer keys than
+    there are new queries, so a tile starts with rows that route to nothing;
+    every other query matches the oracle run on its own sequence."""
+    log(f"case prefill-tiles-ragged paged={paged}")
+    w = Workload("prefill-tiles-ragged", 3, 4, 2, 128, 2048, 150, 128, 32, 3, 6, 1e4, "bf16", 0)
+    seq_lens = [2048, 1000, 100]
+    inp = generate(w)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    if paged:
+        kp, vp, table, n_pages = _pages(w, inp, seq_lens, 64)
+        layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
+        out = _run_ragged(w, inp, seq_lens, layout, kp, vp)
+    else:
+        out = _run_ragged(w, inp, seq_lens, hga.Layout(seq_lens=lens), to_dev(inp.K, w.dtype),
+                          to_dev(inp.V, w.dtype))
+    from synth.inputs import Inputs
+    from tests.gpu_runner import check_ragged
+    check_ragged(w.with_(B=2), inp, seq_lens[:2], {k: v[:2] for k, v in out.items()})
+    Tb, short = seq_lens[2], w.Nq - seq_lens[2]          # queries 0..short-1 sit before key 0
+    assert (out["gidx"][2, :, :short] == -1).all()
     assert (out["O"][2, :, :short] == 0).all() and torch.isinf(out["lse"][2, :, :short]).all()
     wb = w.with_(B=1, T=Tb, Nq=Tb)
     sub = Inputs(wb, inp.seed, inp.Q[2:3, :, short:], inp.K[2:3, :, :Tb], inp.V[2:3, :, :Tb])
