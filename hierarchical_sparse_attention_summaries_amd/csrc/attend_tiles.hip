@@ -32,7 +32,8 @@ constexpr int kTW = 8;                           // waves, 16 rows each
 constexpr int kTThreads = kTW * kWave;
 constexpr int kTG = 32;                          // tokens per group
 constexpr int kTD = 128;                         // head dim
-constexpr int kStageTok = 2 * kTG;               // two groups staged per step
+constexpr int kSG = 4;                           // groups staged per step
+constexpr int kStageTok = kSG * kTG;
 constexpr int kKStride = kTD + 8;                // bf16 per staged K row (padded)
 constexpr int kVStride = kStageTok + 8;          // bf16 per staged V^T row (padded)
 constexpr int kTileMaxGroups = 2048;             // groups of the context (mask rows)
@@ -77,11 +78,11 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) * 4; }
 
 // This thread's share of one step (zeros past the union's end, the context's
-// end, or a page out of range): K of token t / 16 of each of the step's two
-// groups, and V of tokens 2j, 2j + 1 (j = (t % 256) / 16) of group t / 256;
-// dims (t % 16) * 8 .. +7 each.
+// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K of token t / 16
+// of each of the step's groups, and V of tokens 2j, 2j + 1 (j = (t % 256) / 16)
+// of groups t / 256 + 2i.
 struct StepRegs {
-  uint4 k0, k1, v0, v1;
+  uint4 k[kSG], v[kSG];
 };
 
 __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s, int n_u, int b,
@@ -90,37 +91,60 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
   const int col = (t % 16) * 8;
   const uint16_t* K = static_cast<const uint16_t*>(a.K);
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
-  // the global row of token x of the step's group gi, or -1
-  auto row_of = [&](int gi, int x) -> int64_t {
-    const int u = step * 2 + gi;
-    if (u >= n_u) return -1;
-    const int tok = s.list[u] * kTG + x;
-    return tok < a.T ? kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, tok) : -1;
-  };
-  const int64_t k0 = row_of(0, t / 16), k1 = row_of(1, t / 16);
-  const int vg = t / 256, vx = ((t % 256) / 16) * 2;
-  const int64_t v0 = row_of(vg, vx), v1 = row_of(vg, vx + 1);
-  r.k0 = k0 >= 0 ? ld16(K + k0 + col) : make_uint4(0, 0, 0, 0);
-  r.k1 = k1 >= 0 ? ld16(K + k1 + col) : make_uint4(0, 0, 0, 0);
-  r.v0 = v0 >= 0 ? ld16(V + v0 + col) : make_uint4(0, 0, 0, 0);
-  r.v1 = v1 >= 0 ? ld16(V + v1 + col) : make_uint4(0, 0, 0, 0);
+  // where each of the step's groups starts (a group lies within one page), and
+  // how many of its tokens the context holds
+  int64_t base[kSG];
+  int n_tok[kSG];
+#pragma unroll
+  for (int gi = 0; gi < kSG; ++gi) {
+    const int u = step * kSG + gi;
+    base[gi] = -1;
+    n_tok[gi] = 0;
+    if (u < n_u) {
+      const int t0 = s.list[u] * kTG;
+      base[gi] = kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, t0);
+      n_tok[gi] = min(kTG, a.T - t0);
+    }
+  }
+  const int xk = t / 16;
+#pragma unroll
+  for (int gi = 0; gi < kSG; ++gi)
+    r.k[gi] = base[gi] >= 0 && xk < n_tok[gi]
+                  ? ld16(K + base[gi] + static_cast<int64_t>(xk) * kTD + col)
+                  : make_uint4(0, 0, 0, 0);
+  const int xv = ((t % 256) / 16) * 2;
+#pragma unroll
+  for (int pi = 0; pi < kSG / 2; ++pi) {
+    const int gv = t / 256 + 2 * pi;
+#pragma unroll
+    for (int z = 0; z < 2; ++z)
+      r.v[2 * pi + z] = base[gv] >= 0 && xv + z < n_tok[gv]
+                            ? ld16(V + base[gv] + static_cast<int64_t>(xv + z) * kTD + col)
+                            : make_uint4(0, 0, 0, 0);
+  }
 }
 
 __device__ __forceinline__ void stash_step(TileLds& s, const StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
-  *reinterpret_cast<uint4*>(&s.k[(t / 16) * kKStride + col]) = r.k0;
-  *reinterpret_cast<uint4*>(&s.k[(kTG + t / 16) * kKStride + col]) = r.k1;
+#pragma unroll
+  for (int gi = 0; gi < kSG; ++gi)
+    *reinterpret_cast<uint4*>(&s.k[(gi * kTG + t / 16) * kKStride + col]) = r.k[gi];
   // V^T: dims col .. col+7 of tokens x, x + 1 (one 32-bit word each)
-  const int x = (t / 256) * kTG + ((t % 256) / 16) * 2;
-  const uint32_t a0[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w};
-  const uint32_t a1[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
   uint32_t* vt = reinterpret_cast<uint32_t*>(s.vt);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int d = col + 2 * e;
-    vt[(d * kVStride + (x ^ vt_swizzle(d))) / 2] = (a0[e] & 0xffffu) | (a1[e] << 16);
-    vt[((d + 1) * kVStride + (x ^ vt_swizzle(d + 1))) / 2] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+  for (int pi = 0; pi < kSG / 2; ++pi) {
+    const int x = (t / 256 + 2 * pi) * kTG + ((t % 256) / 16) * 2;
+    const uint4 v0 = r.v[2 * pi], v1 = r.v[2 * pi + 1];
+    const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
+    const uint32_t a1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = col + 2 * e;
+      vt[(d * kVStride + (x ^ vt_swizzle(d))) / 2] = (a0[e] & 0xffffu) | (a1[e] << 16);
+      vt[((d + 1) * kVStride + (x ^ vt_swizzle(d + 1))) / 2] =
+          (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+    }
   }
 }
 
@@ -195,19 +219,25 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   for (int d = 0; d < kTD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  // One step: two groups of the union, staged in LDS.
+  // One step: kSG groups of the union, staged in LDS.
   auto compute = [&](int step) {
-    const int u0 = step * 2;
-    const int g0 = s.list[u0];
-    const int g1 = u0 + 1 < n_u ? s.list[u0 + 1] : -1;
-    const uint32_t bits0 = (s.mask[g0][mword] >> mshift) & 0xFFFFu;
-    const uint32_t bits1 = g1 >= 0 ? (s.mask[g1][mword] >> mshift) & 0xFFFFu : 0u;
-    if ((bits0 | bits1) == 0u) return;  // none of the wave's rows takes these groups
-    // S^T: 4 blocks of 16 tokens x the wave's 16 rows
-    f32x4 sacc[4];
+    int g[kSG];
+    uint32_t bits[kSG];
+    uint32_t any = 0u;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int gi = 0; gi < kSG; ++gi) {
+      const int u = step * kSG + gi;
+      g[gi] = u < n_u ? s.list[u] : -1;
+      bits[gi] = g[gi] >= 0 ? (s.mask[g[gi]][mword] >> mshift) & 0xFFFFu : 0u;
+      any |= bits[gi];
+    }
+    if (any == 0u) return;  // none of the wave's rows takes these groups
+    // S^T: 2 blocks of 16 tokens per group x the wave's 16 rows
+    f32x4 sacc[2 * kSG];
+#pragma unroll
+    for (int tb = 0; tb < 2 * kSG; ++tb) {
       sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (bits[tb / 2] == 0u) continue;  // uniform over the wave
 #pragma unroll
       for (int ks = 0; ks < kTD / 32; ++ks) {
         const uint4 ka = *reinterpret_cast<const uint4*>(
@@ -218,18 +248,19 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     }
     // mask (routed group, causal) and scale to base 2: token x of group g is
     // taken iff the row routed g and x <= p - g * G
-    const int lim0 = (row_ok && ((bits0 >> (lane % 16)) & 1u)) ? p_r - g0 * kTG : -1;
-    const int lim1 = (row_ok && ((bits1 >> (lane % 16)) & 1u)) ? p_r - g1 * kTG : -1;
-    float sv[4][4];
+    float sv[2 * kSG][4];
     float mt = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int lim = tb < 2 ? lim0 : lim1;
+    for (int gi = 0; gi < kSG; ++gi) {
+      const int lim = (row_ok && ((bits[gi] >> (lane % 16)) & 1u)) ? p_r - g[gi] * kTG : -1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[tb][i] = ((tb & 1) * 16 + a4 + i <= lim) ? sacc[tb][i] * sl2 : -INFINITY;
-        mt = fmaxf(mt, sv[tb][i]);
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tb = 2 * gi + h2;
+          sv[tb][i] = (h2 * 16 + a4 + i <= lim) ? sacc[tb][i] * sl2 : -INFINITY;
+          mt = fmaxf(mt, sv[tb][i]);
+        }
     }
     mt = pair_max<16>(mt);
     mt = pair_max<32>(mt);
@@ -243,26 +274,19 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     }
     m = m_new;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // rows with nothing yet: p = 0
-    float p[4][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[tb][i] = __builtin_amdgcn_exp2f(sv[tb][i] - m_use);
-        l += p[tb][i];
-      }
     // O^T += V^T . P^T, one group at a time, P as bf16 hi + lo
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      if ((gi == 0 ? bits0 : bits1) == 0u) continue;  // uniform over the wave
+    for (int gi = 0; gi < kSG; ++gi) {
+      if (bits[gi] == 0u) continue;  // uniform over the wave
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(sv[2 * gi + j / 4][j % 4] - m_use);
+        l += p[j];
+      }
       uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 2 * e;  // operand slots j, j + 1: tokens of block 2gi (j < 4) or 2gi + 1
-        const float x0 = j < 4 ? p[2 * gi][j] : p[2 * gi + 1][j - 4];
-        const float x1 = j < 4 ? p[2 * gi][j + 1] : p[2 * gi + 1][j - 3];
-        split_pair(x0, x1, hw[e], lw[e]);
-      }
+      for (int e = 0; e < 4; ++e) split_pair(p[2 * e], p[2 * e + 1], hw[e], lw[e]);
       const bf16x8 ph = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
       const bf16x8 pl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
@@ -279,29 +303,17 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     }
   };
 
-  // 4. The union in steps of two groups. One workgroup per CU (its LDS), so
-  // each step's loads go out four steps ahead of its use: 128 KiB in flight.
-  const int n_st = (n_u + 1) / 2;
-  StepRegs r0, r1, r2, r3;
-  fetch_step(a, s, n_u, b, kv, 0, r0);
-  fetch_step(a, s, n_u, b, kv, 1, r1);
-  fetch_step(a, s, n_u, b, kv, 2, r2);
-  fetch_step(a, s, n_u, b, kv, 3, r3);
-  auto step = [&](int st, StepRegs& r) {
+  // 4. The union in steps of kSG groups. One workgroup per CU (its LDS); each
+  // step's loads go out one step ahead of its use (64 KiB in flight).
+  const int n_st = (n_u + kSG - 1) / kSG;
+  StepRegs r;
+  fetch_step(a, s, n_u, b, kv, 0, r);
+  for (int st = 0; st < n_st; ++st) {
     stash_step(s, r);
     lds_barrier();
-    fetch_step(a, s, n_u, b, kv, st + 4, r);
+    fetch_step(a, s, n_u, b, kv, st + 1, r);
     compute(st);
     lds_barrier();
-  };
-  for (int st = 0; st < n_st; st += 4) {
-    step(st, r0);
-    if (st + 1 >= n_st) break;
-    step(st + 1, r1);
-    if (st + 2 >= n_st) break;
-    step(st + 2, r2);
-    if (st + 3 >= n_st) break;
-    step(st + 3, r3);
   }
 
   // 5. The row's total over its 4 lanes; each lane writes its 32 dims.
