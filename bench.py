@@ -231,6 +231,30 @@ def measure(w, args, primary: bool):
     # gathers then hit in cache, and the per-row gathers are reported apart.
     attend_bytes = union_tokens * w.D * 2 * esize + rows * (2 * w.D * esize + 4 * w.k_group + 4)
     gather_bytes = routed_tokens * w.D * 2 * esize
+    # Many queries per head (bf16, D 128, G 32, <= 2048 groups, >= 128 queries):
+    # the attention runs in tiles of 128 rows of one head over the union of
+    # their routed groups, on MFMA. Its bytes are each tile's union; its
+    # executed MFMA work counts, for every 16-row wave, every group any of
+    # its rows routed: 16 rows x 32 tokens x D for S^T, twice that for the
+    # hi + lo products of O^T, 2 flops each.
+    tiles = None
+    if (w.dtype == "bf16" and w.D == 128 and w.group == 32 and w.n_groups <= 2048
+            and w.Nq >= 128):
+        n_union = n_wave_groups = n_tiles = 0
+        for b in range(w.B):
+            for h in range(w.Hq):
+                for i0 in range(0, w.Nq, 128):
+                    blk = g[b, h, i0:i0 + 128]
+                    n_union += len(np.unique(blk[blk >= 0]))
+                    n_tiles += 1
+                    for w0 in range(0, blk.shape[0], 16):
+                        wb = blk[w0:w0 + 16]
+                        n_wave_groups += len(np.unique(wb[wb >= 0]))
+        tiles = {"tiles": n_tiles, "union_groups_per_tile": round(n_union / n_tiles, 1),
+                 "bytes": n_union * w.group * w.D * 2 * esize
+                 + rows * (2 * w.D * esize + 4 * w.k_group + 4),
+                 "executed_flops": n_wave_groups * 16 * w.group * w.D * 2 * 3,
+                 "alg_flops": routed_tokens * w.D * 4}
     # One decode step: Q, all chunk summaries, the candidate groups' summaries,
     # the routed K/V (union per KV head), O, lse and ids, plus the refresh of the
     # chunks holding the newest keys (their keys read, their summaries written).
@@ -473,6 +497,20 @@ def measure(w, args, primary: bool):
     roofline_attend = roof("attend", attend_bytes, attend_us)
     roofline_attend["gathered_bytes_per_launch"] = gather_bytes
     roofline_attend["gathered_gbs"] = round(gather_bytes / (attend_us * 1e-6) / 1e9, 1)
+    if tiles is not None:
+        # the tile kernel is a (masked) MFMA contraction: its executed flops
+        # against the dense bf16 peak; its bytes (each tile's union) beside
+        tf = tiles["executed_flops"] / (attend_us * 1e-6) / 1e12
+        roofline_attend = {
+            "kernel": "hga_attend_tiles", "bound": "mfma", "achieved": round(tf, 1),
+            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+            "executed_flops_per_launch": tiles["executed_flops"],
+            "alg_flops_per_launch": tiles["alg_flops"],
+            "bytes_per_launch": tiles["bytes"],
+            "gbs": round(tiles["bytes"] / (attend_us * 1e-6) / 1e9, 1),
+            "tiles": tiles["tiles"], "union_groups_per_tile": tiles["union_groups_per_tile"],
+            "avg_launch_us": round(attend_us, 3)}
     roofline_step = roof("decode_step", step_bytes, decode_us)
     roofline_step["launches"] = 1 if decode_one_launch else 2
     roofline = dict(roofline_step if decode_one_launch else roofline_attend)
