@@ -8,14 +8,15 @@
 // on MFMA 16x16x32 bf16, masking per row: a row takes a group's tokens only if
 // it routed the group, and only up to its own position.
 //
-// Layout, per wave (16 rows): S^T = K . Q^T with K rows as the A operand and
-// the wave's query rows as B, so that each lane ends up with 8 scores of one
-// row (two 16-token blocks of a group); the online softmax keeps (m, l) per row
-// in the 4 lanes that hold it; O^T = V^T . P^T with the staged V^T as A and the
-// lane's own probabilities as B (the 32 tokens of a group in the lane order
-// the scores came in), so each lane accumulates 32 dims of its own row and the
-// rescaling stays lane-local. P enters the product as bf16 hi + lo parts, so
-// the accumulation carries P to about 2^-17 relative.
+// Layout, per 16-row block of a wave (a wave has two): S^T = K . Q^T with K
+// rows as the A operand and the block's query rows as B, so that each lane
+// ends up with 8 scores of one row per group (two 16-token blocks); the online
+// softmax keeps (m, l) per row in the 4 lanes that hold it; O^T = V^T . P^T
+// with the staged V^T as A and the lane's own probabilities as B (the 32
+// tokens of a group in the lane order the scores came in), so each lane
+// accumulates 32 dims of its own row and the rescaling stays lane-local. One
+// operand read from LDS serves both row blocks. P enters the product as bf16
+// hi + lo parts, so the accumulation carries P to about 2^-17 relative.
 #include <math.h>
 
 #include "hga_device.h"
@@ -27,16 +28,21 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTR = 128;                         // query rows per tile (workgroup)
-constexpr int kTW = 8;                           // waves, 16 rows each
+constexpr int kTW = 4;                           // waves per workgroup
+constexpr int kRB = 2;                           // 16-row blocks per wave
+constexpr int kTR = kTW * kRB * 16;              // query rows per tile (workgroup): 128
 constexpr int kTThreads = kTW * kWave;
 constexpr int kTG = 32;                          // tokens per group
 constexpr int kTD = 128;                         // head dim
-constexpr int kSG = 4;                           // groups staged per step
+constexpr int kSG = 1;                           // groups staged per step
 constexpr int kStageTok = kSG * kTG;
 constexpr int kKStride = kTD + 8;                // bf16 per staged K row (padded)
 constexpr int kVStride = kStageTok + 8;          // bf16 per staged V^T row (padded)
 constexpr int kTileMaxGroups = 2048;             // groups of the context (mask rows)
+constexpr int kNK = kSG * kTG * 16 / kTThreads;  // K loads per thread per step
+constexpr int kNV = kSG * 16 * 16 / kTThreads;   // V token pairs per thread per step
+static_assert(kNK >= 1 && kNV >= 1, "every thread loads K and V");
+static_assert(kTR == 32 * kTW, "one 32-bit mask word per wave");
 
 struct TileLds {
   uint32_t mask[kTileMaxGroups][kTR / 32];       // rows of the tile that routed each group
@@ -44,7 +50,6 @@ struct TileLds {
   alignas(16) uint16_t k[kStageTok * kKStride];  // staged K rows
   alignas(16) uint16_t vt[kTD * kVStride];       // staged V^T
   int wave_count[kTW];
-  int n_union;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
@@ -64,8 +69,7 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
 }
 
 // Workgroup barrier ordering LDS only: unlike __syncthreads(), it does not
-// wait for this thread's global loads, so loads issued steps ahead stay in
-// flight across it.
+// wait for this thread's global loads, so loads issued ahead stay in flight.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -78,11 +82,11 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) * 4; }
 
 // This thread's share of one step (zeros past the union's end, the context's
-// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K of token t / 16
-// of each of the step's groups, and V of tokens 2j, 2j + 1 (j = (t % 256) / 16)
-// of groups t / 256 + 2i.
+// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K of step tokens
+// t / 16 + n * (threads / 16), and V of token pairs 2j, 2j + 1 of the step's
+// group pairs t / 16 + n * (threads / 16) (16 pairs per group).
 struct StepRegs {
-  uint4 k[kSG], v[kSG];
+  uint4 k[kNK], v[2 * kNV];
 };
 
 __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s, int n_u, int b,
@@ -106,21 +110,23 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
       n_tok[gi] = min(kTG, a.T - t0);
     }
   }
-  const int xk = t / 16;
 #pragma unroll
-  for (int gi = 0; gi < kSG; ++gi)
-    r.k[gi] = base[gi] >= 0 && xk < n_tok[gi]
-                  ? ld16(K + base[gi] + static_cast<int64_t>(xk) * kTD + col)
-                  : make_uint4(0, 0, 0, 0);
-  const int xv = ((t % 256) / 16) * 2;
+  for (int n = 0; n < kNK; ++n) {
+    const int tg = t / 16 + n * (kTThreads / 16);  // step token
+    const int gi = tg / kTG, x = tg % kTG;
+    r.k[n] = base[gi] >= 0 && x < n_tok[gi]
+                 ? ld16(K + base[gi] + static_cast<int64_t>(x) * kTD + col)
+                 : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-  for (int pi = 0; pi < kSG / 2; ++pi) {
-    const int gv = t / 256 + 2 * pi;
+  for (int n = 0; n < kNV; ++n) {
+    const int pg = t / 16 + n * (kTThreads / 16);  // step token pair
+    const int gi = pg / 16, x = (pg % 16) * 2;
 #pragma unroll
     for (int z = 0; z < 2; ++z)
-      r.v[2 * pi + z] = base[gv] >= 0 && xv + z < n_tok[gv]
-                            ? ld16(V + base[gv] + static_cast<int64_t>(xv + z) * kTD + col)
-                            : make_uint4(0, 0, 0, 0);
+      r.v[2 * n + z] = base[gi] >= 0 && x + z < n_tok[gi]
+                           ? ld16(V + base[gi] + static_cast<int64_t>(x + z) * kTD + col)
+                           : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -128,14 +134,14 @@ __device__ __forceinline__ void stash_step(TileLds& s, const StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
 #pragma unroll
-  for (int gi = 0; gi < kSG; ++gi)
-    *reinterpret_cast<uint4*>(&s.k[(gi * kTG + t / 16) * kKStride + col]) = r.k[gi];
+  for (int n = 0; n < kNK; ++n)
+    *reinterpret_cast<uint4*>(&s.k[(t / 16 + n * (kTThreads / 16)) * kKStride + col]) = r.k[n];
   // V^T: dims col .. col+7 of tokens x, x + 1 (one 32-bit word each)
   uint32_t* vt = reinterpret_cast<uint32_t*>(s.vt);
 #pragma unroll
-  for (int pi = 0; pi < kSG / 2; ++pi) {
-    const int x = (t / 256 + 2 * pi) * kTG + ((t % 256) / 16) * 2;
-    const uint4 v0 = r.v[2 * pi], v1 = r.v[2 * pi + 1];
+  for (int n = 0; n < kNV; ++n) {
+    const int x = (t / 16 + n * (kTThreads / 16)) * 2;  // step token of the pair
+    const uint4 v0 = r.v[2 * n], v1 = r.v[2 * n + 1];
     const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
     const uint32_t a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   __syncthreads();
 
   // 2. The union of the tile's groups, ascending: slot j covers groups
-  // [j * kTThreads, +kTThreads), one per thread.
+  // [j * threads, +threads), one per thread.
   int n_u = 0;
   for (int base = 0; base < n_g; base += kTThreads) {
     const int g = base + tid;
@@ -199,96 +205,127 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     __syncthreads();
   }
 
-  // 3. This lane's query row (one of the wave's 16) as the B operand.
+  // 3. This lane's query rows (one in each of the wave's 16-row blocks) as B
+  // operands; tile row of block rb: wave * 32 + rb * 16 + lane % 16.
   const int a8 = (lane / 16) * 8;          // k offset of this lane's operand slice
   const int a4 = (lane / 16) * 4;          // token / dim offset of its result slice
-  const int my_r = wave * 16 + lane % 16;  // tile row
-  const bool row_ok = my_r < nrows;
-  const int p_r = Tb - a.Nq + i0 + my_r;   // its position (rows past the tile: unused)
-  uint4 qB[kTD / 32];
+  bool row_ok[kRB];
+  int p_r[kRB];
+  uint4 qB[kRB][kTD / 32];
 #pragma unroll
-  for (int ks = 0; ks < kTD / 32; ++ks) {
-    qB[ks] = row_ok ? ld16(static_cast<const uint16_t*>(a.Q) + (row0 + my_r) * kTD + ks * 32 + a8)
-                    : make_uint4(0, 0, 0, 0);
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int my_r = wave * 32 + rb * 16 + lane % 16;
+    row_ok[rb] = my_r < nrows;
+    p_r[rb] = Tb - a.Nq + i0 + my_r;       // its position (rows past the tile: unused)
+#pragma unroll
+    for (int ks = 0; ks < kTD / 32; ++ks)
+      qB[rb][ks] = row_ok[rb] ? ld16(static_cast<const uint16_t*>(a.Q) + (row0 + my_r) * kTD +
+                                     ks * 32 + a8)
+                              : make_uint4(0, 0, 0, 0);
   }
   const float sl2 = a.scale * kLog2e;
-  const int mword = wave >> 1, mshift = (wave & 1) * 16;
 
-  f32x4 o[kTD / 16];
+  f32x4 o[kRB][kTD / 16];
 #pragma unroll
-  for (int d = 0; d < kTD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int d = 0; d < kTD / 16; ++d) o[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[kRB], l[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
 
   // One step: kSG groups of the union, staged in LDS.
   auto compute = [&](int step) {
     int g[kSG];
-    uint32_t bits[kSG];
+    uint32_t bits[kSG];  // the wave's 32 rows that routed each group
     uint32_t any = 0u;
 #pragma unroll
     for (int gi = 0; gi < kSG; ++gi) {
       const int u = step * kSG + gi;
       g[gi] = u < n_u ? s.list[u] : -1;
-      bits[gi] = g[gi] >= 0 ? (s.mask[g[gi]][mword] >> mshift) & 0xFFFFu : 0u;
+      bits[gi] = g[gi] >= 0 ? s.mask[g[gi]][wave] : 0u;
       any |= bits[gi];
     }
     if (any == 0u) return;  // none of the wave's rows takes these groups
-    // S^T: 2 blocks of 16 tokens per group x the wave's 16 rows
-    f32x4 sacc[2 * kSG];
+    // S^T: 2 blocks of 16 tokens per group x each 16-row block; one K operand
+    // read serves both row blocks
+    f32x4 sacc[2 * kSG][kRB];
 #pragma unroll
     for (int tb = 0; tb < 2 * kSG; ++tb) {
-      sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sacc[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (bits[tb / 2] == 0u) continue;  // uniform over the wave
 #pragma unroll
       for (int ks = 0; ks < kTD / 32; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(
-            &s.k[(tb * 16 + lane % 16) * kKStride + ks * 32 + a8]);
-        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qB[ks]),
-                                                           sacc[tb], 0, 0, 0);
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &s.k[(tb * 16 + lane % 16) * kKStride + ks * 32 + a8]));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          sacc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(qB[rb][ks]),
+                                                                 sacc[tb][rb], 0, 0, 0);
       }
     }
-    // mask (routed group, causal) and scale to base 2: token x of group g is
-    // taken iff the row routed g and x <= p - g * G
-    float sv[2 * kSG][4];
-    float mt = -INFINITY;
+    // Per row block: mask (routed group, causal), base-2 scale, online softmax.
+    // Token x of group g is taken iff the row routed g and x <= p - g * G.
+    float p[kRB][2 * kSG][4];
 #pragma unroll
-    for (int gi = 0; gi < kSG; ++gi) {
-      const int lim = (row_ok && ((bits[gi] >> (lane % 16)) & 1u)) ? p_r - g[gi] * kTG : -1;
+    for (int rb = 0; rb < kRB; ++rb) {
+      float mt = -INFINITY;
+      float sv[2 * kSG][4];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int gi = 0; gi < kSG; ++gi) {
+        const bool in = row_ok[rb] && ((bits[gi] >> (rb * 16 + lane % 16)) & 1u);
+        const int lim = in ? p_r[rb] - g[gi] * kTG : -1;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tb = 2 * gi + h2;
+            sv[tb][i] = (h2 * 16 + a4 + i <= lim) ? sacc[tb][rb][i] * sl2 : -INFINITY;
+            mt = fmaxf(mt, sv[tb][i]);
+          }
+      }
+      mt = pair_max<16>(mt);
+      mt = pair_max<32>(mt);
+      const float m_new = fmaxf(m[rb], mt);
+      // rescale only where a row's running maximum moved (rarely, once warm)
+      if (ballot(m_new > m[rb]) != 0u) {
+        const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
+        l[rb] *= corr;
+#pragma unroll
+        for (int d = 0; d < kTD / 16; ++d) o[rb][d] *= corr;
+      }
+      m[rb] = m_new;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // rows with nothing yet: p = 0
+#pragma unroll
+      for (int tb = 0; tb < 2 * kSG; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tb = 2 * gi + h2;
-          sv[tb][i] = (h2 * 16 + a4 + i <= lim) ? sacc[tb][i] * sl2 : -INFINITY;
-          mt = fmaxf(mt, sv[tb][i]);
+          p[rb][tb][i] = __builtin_amdgcn_exp2f(sv[tb][i] - m_use);
+          l[rb] += p[rb][tb][i];
         }
     }
-    mt = pair_max<16>(mt);
-    mt = pair_max<32>(mt);
-    const float m_new = fmaxf(m, mt);
-    // rescale only where a row's running maximum moved (rarely, once warm)
-    if (ballot(m_new > m) != 0u) {
-      const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-      l *= corr;
-#pragma unroll
-      for (int d = 0; d < kTD / 16; ++d) o[d] *= corr;
-    }
-    m = m_new;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // rows with nothing yet: p = 0
-    // O^T += V^T . P^T, one group at a time, P as bf16 hi + lo
+    // O^T += V^T . P^T, one group at a time, P as bf16 hi + lo; one V^T
+    // operand read serves both row blocks
 #pragma unroll
     for (int gi = 0; gi < kSG; ++gi) {
       if (bits[gi] == 0u) continue;  // uniform over the wave
-      float p[8];
+      bf16x8 ph[kRB], pl[kRB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sv[2 * gi + j / 4][j % 4] - m_use);
-        l += p[j];
+      for (int rb = 0; rb < kRB; ++rb) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 2 * e;  // operand slots j, j + 1: block 2gi (j < 4) or 2gi + 1
+          split_pair(p[rb][2 * gi + j / 4][j % 4], p[rb][2 * gi + j / 4][j % 4 + 1], hw[e],
+                     lw[e]);
+        }
+        ph[rb] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pl[rb] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split_pair(p[2 * e], p[2 * e + 1], hw[e], lw[e]);
-      const bf16x8 ph = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8 pl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
       for (int d = 0; d < kTD / 16; ++d) {
         const int dim = d * 16 + lane % 16;
@@ -297,43 +334,58 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
         const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + a4) ^ sw));
         const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + 16 + a4) ^ sw));
         const bf16x8 va = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, o[d], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[rb], o[rb][d], 0, 0, 0);
+          o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb], o[rb][d], 0, 0, 0);
+        }
       }
     }
   };
 
-  // 4. The union in steps of kSG groups. One workgroup per CU (its LDS); each
-  // step's loads go out one step ahead of its use (64 KiB in flight).
+  // 4. The union in steps of kSG groups; each step's loads go out two steps
+  // ahead of its use (two workgroups per CU: 64 KiB in flight).
   const int n_st = (n_u + kSG - 1) / kSG;
-  StepRegs r;
-  fetch_step(a, s, n_u, b, kv, 0, r);
-  for (int st = 0; st < n_st; ++st) {
-    stash_step(s, r);
+  StepRegs r0, r1;
+  fetch_step(a, s, n_u, b, kv, 0, r0);
+  fetch_step(a, s, n_u, b, kv, 1, r1);
+  for (int st = 0; st < n_st; st += 2) {
+    stash_step(s, r0);
     lds_barrier();
-    fetch_step(a, s, n_u, b, kv, st + 1, r);
+    fetch_step(a, s, n_u, b, kv, st + 2, r0);
     compute(st);
+    lds_barrier();
+    if (st + 1 >= n_st) break;
+    stash_step(s, r1);
+    lds_barrier();
+    fetch_step(a, s, n_u, b, kv, st + 3, r1);
+    compute(st + 1);
     lds_barrier();
   }
 
-  // 5. The row's total over its 4 lanes; each lane writes its 32 dims.
-  l = pair_sum<16>(l);
-  l = pair_sum<32>(l);
-  if (row_ok) {
-    const size_t orow = (row0 + my_r) * kTD;
-    uint16_t* O = static_cast<uint16_t*>(a.O);
+  // 5. Each row's total over its 4 lanes; each lane writes 32 dims of its rows.
 #pragma unroll
-    for (int d = 0; d < kTD / 16; ++d) {
-      uint32_t w[2];
+  for (int rb = 0; rb < kRB; ++rb) {
+    float lt = pair_sum<16>(l[rb]);
+    lt = pair_sum<32>(lt);
+    if (row_ok[rb]) {
+      const int my_r = wave * 32 + rb * 16 + lane % 16;
+      const size_t orow = (row0 + my_r) * kTD;
+      uint16_t* O = static_cast<uint16_t*>(a.O);
 #pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const float v0 = l > 0.f ? o[d][2 * z] / l : 0.f;
-        const float v1 = l > 0.f ? o[d][2 * z + 1] / l : 0.f;
-        w[z] = bf16_bits(v0) | (bf16_bits(v1) << 16);
+      for (int d = 0; d < kTD / 16; ++d) {
+        uint32_t w[2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const float v0 = lt > 0.f ? o[rb][d][2 * z] / lt : 0.f;
+          const float v1 = lt > 0.f ? o[rb][d][2 * z + 1] / lt : 0.f;
+          w[z] = bf16_bits(v0) | (bf16_bits(v1) << 16);
+        }
+        *reinterpret_cast<uint2*>(O + orow + d * 16 + a4) = make_uint2(w[0], w[1]);
       }
-      *reinterpret_cast<uint2*>(O + orow + d * 16 + a4) = make_uint2(w[0], w[1]);
+      if (a.lse && lane < 16)
+        a.lse[row0 + my_r] = lt > 0.f ? (m[rb] + log2f(lt)) * kLn2 : -INFINITY;
     }
-    if (a.lse && lane < 16) a.lse[row0 + my_r] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
