@@ -8,7 +8,9 @@ beyond the score margin, ε-valid choices, outputs within tolerance). Shapes
 with many query rows per KV head take the MFMA prefill route, small ones the
 one-workgroup-per-row route, the rest the multi-workgroup route. Cases whose
 newest queries fit one chunk also run the one-call decode step and compare it
-with the separate calls.
+with the separate calls. The last few draw at least 128 queries per sequence in
+bf16 with D = 128 and G = 32, so that their attention runs in 128-row tiles
+over the union of routed groups (partial last tiles included).
 """
 import numpy as np
 import pytest
@@ -22,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 28
 N_MANY_ROWS = 4   # the last cases: > 1024 query rows, not the MFMA route
+N_TILES = 6       # then: the tile attention
 
 
 def draw(seed):
@@ -53,15 +56,27 @@ def draw(seed):
     return Workload(f"random-{seed}", B, r * Hkv, Hkv, D, T, Nq, C, G, k_c, k_g, 1e4, dtype, 0)
 
 
+def draw_tiles(seed):
+    rng = np.random.default_rng(2000 + seed)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2]))
+    r = int(rng.choice([1, 2, 4, 8]))
+    C = 32 * int(rng.choice([1, 2, 4, 8]))
+    Nq = int(rng.integers(128, 401))
+    T = int(rng.integers(max(C, Nq), 3072))
+    return Workload(f"random-tiles-{seed}", B, r * Hkv, Hkv, 128, T, Nq, C, 32,
+                    int(rng.integers(0, 7)), int(rng.integers(1, 24)), 1e4, "bf16", 0)
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+@pytest.mark.parametrize("seed", range(N_CASES + N_TILES))
 def test_random_shape(seed):
-    w = draw(seed)
+    w = draw(seed) if seed < N_CASES else draw_tiles(seed - N_CASES)
     log(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T={w.T} Nq={w.Nq} "
         f"C={w.chunk} G={w.group} k_c={w.k_chunk} k_g={w.k_group} {w.dtype}")
     inp = generate(w)
