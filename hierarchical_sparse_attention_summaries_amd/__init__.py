@@ -21,7 +21,7 @@ __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summa
            "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
            "Layout", "build_summaries_ex", "update_summaries_ex", "route_ex", "attend_ex",
            "route_fresh_ex",
-           "LIB_PATH"]
+           "LIB_PATH", "WORKSPACE_ZERO_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
 
@@ -85,6 +85,7 @@ def _load():
     P = ctypes.POINTER
     sig = {
         "hga_abi_version": (ctypes.c_int, []),
+        "hga_workspace_zero_bytes": (ctypes.c_size_t, []),
         "hga_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "hga_summary_counts": (ctypes.c_int, [i64, i32, i32, P(i64), P(i64)]),
         "hga_build_summaries": (ctypes.c_int, [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp]),
@@ -122,6 +123,9 @@ def _load():
 
 
 _lib = _load()
+# Bytes at the start of every workspace that must be zero before its first use
+# (every call leaves them at zero).
+WORKSPACE_ZERO_BYTES = int(_lib.hga_workspace_zero_bytes())
 
 
 def lib():
@@ -161,7 +165,7 @@ def _ptr(t):
 
 
 # Zero-initialised workspaces, one per (device, role), grown on demand. The
-# library leaves their counters at zero after each call.
+# library leaves their zero region at zero after each call.
 _ws_lock = threading.Lock()
 _ws: dict = {}
 

@@ -141,9 +141,8 @@ bool row_fresh_fused(const hga_shape* s, int32_t dtype, int32_t chunk, int32_t g
 }
 
 // Counter words of the one-launch decode step: the attention's split counters
-// sit at [kDecodeAttendCounters, +rows) (rows <= the CU count there), clear of
-// the per-unit scoring counters below them.
-constexpr int kDecodeAttendCounters = 8192;
+// sit at [kDecodeAttendCounters, +rows) (rows <= the CU count there).
+constexpr int kDecodeAttendCounters = 0;
 
 // Whether hga_decode_step_ex runs as one launch (small batches).
 bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
@@ -154,7 +153,8 @@ bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t
 
 // Workspace of hga_decode_step_ex: the larger of the two-call form (routing,
 // then attention in stream order over the same workspace) and the one-launch
-// form (the attention's counters and partials, then every row's scores).
+// form (the attention's counters and partials; the rows' score words sit in
+// the zero-at-rest region every workspace begins with).
 size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
                               int32_t k_group) {
   const int64_t rows = s->batch * s->q_heads * s->n_queries;
@@ -162,8 +162,8 @@ size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, 
                                    chunk, group, k_chunk, k_group)
                        .bytes,
                    hga::plan_attend(rows, s->head_dim, group, k_group).bytes,
-                   hga::decode_step_bytes(s->batch, s->q_heads, s->n_queries, s->seq_len,
-                                          s->head_dim, chunk, group, k_group)});
+                   hga::decode_step_bytes(s->batch, s->q_heads, s->n_queries, s->head_dim,
+                                          k_group)});
 }
 
 // Checks a caller's K/V layout against the capacity T and group size and
@@ -192,6 +192,8 @@ int to_layout(const hga_kv_layout* in, int64_t T, int32_t group, hga::KvLayout* 
 extern "C" {
 
 int hga_abi_version(void) { return HGA_ABI_VERSION; }
+
+size_t hga_workspace_zero_bytes(void) { return hga::kZeroBytes; }
 
 const char* hga_status_str(int status) {
   switch (status) {

@@ -56,7 +56,7 @@ AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves) {
   const int waves_per_row = (k_g + gpw - 1) / gpw;
   pl.n_splits = (waves_per_row + waves - 1) / waves;
   pl.off_counters = 0;
-  pl.off_partials = kCounterBytes;
+  pl.off_partials = kZeroBytes;
   const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;
   pl.bytes = align_up(pl.off_partials + part, 256);
   return pl;

@@ -11,18 +11,19 @@
 // every group, so that no level waits for the other. Item 0 of a unit
 // recomputes the chunks holding the sequence's newest keys from K (same bits
 // as the summaries kernel), writes them out and scores them; the others split
-// the older summaries evenly. Scores go to the workspace with agent-coherent
-// stores, and the item then raises a flag word of its own (no counter that
-// many workgroups bump one after another). Scoring never waits.
+// the older summaries evenly. Scores go to the workspace's zero-at-rest region
+// with agent-coherent stores, as words that are never zero (score_word), so a
+// score that has arrived is its own ready signal: no flag, no wait for the
+// stores to be acknowledged, no second read. Scoring never waits.
 //
-// Attention item (workgroups [0, rows * n_splits)): wave 0 polls the flags of
-// its row's unit (one word per lane per load, bounded), the workgroup pulls
-// the row's scores into LDS, and wave 0 makes the row's two-level selection
-// (every split of the row chooses the same ids from the same scores); then 8
-// waves gather the split's share of the routed keys and values. Split 0
-// writes the row's ids out. The workgroup that finishes a row counts it in on
-// the unit's counter; the unit's last row clears the unit's flags and counter
-// for the next call.
+// Attention item (workgroups [0, rows * n_splits)): the workgroup polls its
+// row's score words (bounded) until none is zero and decodes them into LDS,
+// and wave 0 makes the row's two-level selection (every split of the row
+// chooses the same ids from the same scores); then 8 waves gather the split's
+// share of the routed keys and values. Split 0 writes the row's ids out. The
+// workgroup that finishes a row (every split has counted itself in, so every
+// split has read the row's scores) zeroes the row's score words for the next
+// call.
 //
 // Against one workgroup per query row running both levels back to back, this
 // reads every group summary (not only the candidates'), spread over every CU,
@@ -37,31 +38,42 @@ namespace {
 using rowroute::kThreads;
 using rowroute::kWaves;
 
-// Counter words of the step (the workspace's first kCounterBytes): scoring
-// flags at [kUnitFlags, +U * items) (U * items <= the CU count), rows done per
-// unit at [kUnitDone, +U); the attention's split counters are passed in
-// separately.
-constexpr int kUnitFlags = 0;
-constexpr int kUnitDone = 4096;
-
 struct StepArgs {
-  float* scores;      // [rows, n_c + n_g]: chunk scores, then group scores
-  unsigned* flags;    // [U, items]: a scoring item's stores are performed
-  unsigned* done;     // per unit: rows finished
+  int32_t* scores;    // [rows, n_c + n_g] score words (chunks, then groups); zero at rest
   int items;          // scoring items per unit (>= 2)
   int n_splits;       // attention workgroups per row
   int groups_per_wave;
 };
 
+// A score as a workspace word: the bits of s + 0 (so never -0) with the sign
+// bit flipped, which is never zero; zero marks a score not written yet. The
+// round trip gives s, or +0 for -0, which has the same selection key.
+__device__ __forceinline__ int32_t score_word(float s) {
+  return __float_as_int(s + 0.0f) ^ static_cast<int32_t>(0x80000000u);
+}
+__device__ __forceinline__ float score_of_word(int32_t w) {
+  return __int_as_float(w ^ static_cast<int32_t>(0x80000000u));
+}
+
+// Score words a scoring pass writes for each query row of a unit whose
+// sequence holds Tb > 0 keys: chunks [0, n_chunks), groups [0, n_groups).
+__device__ __forceinline__ void written_range(const RouteArgs& a, int Tb, int& n_chunks,
+                                              int& n_groups) {
+  const int cl = (Tb - 1) / a.C;
+  n_chunks = cl + 1;
+  n_groups = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G);
+}
+
 // Scores summary rows i in [0, n) (row_ptr(i): D floats, all of one pointer
 // kind) against query rows row0 .. row0 + nq - 1: the score of query row j and
-// summary row i goes to scores[(row0 + j) * NS + col_of(i)]. Lane l of wave w
+// summary row i goes to scores[(row0 + j) * NS + col_of(i)] as a score word. Lane l of wave w
 // holds dims [(l % LPR) * 8, +8) of summary rows w * RPS + l / LPR + k * kStride;
 // the dot product is the row route's, in the same order, so both give the same
 // bits.
 template <typename TQ, int D, typename RowPtr, typename ColOf>
 __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq, int n,
-                                            RowPtr row_ptr, ColOf col_of, float* scores, int NS) {
+                                            RowPtr row_ptr, ColOf col_of, int32_t* scores,
+                                            int NS) {
   constexpr int LPR = D / 8;
   constexpr int RPS = kWave / LPR;
   constexpr int kStride = kWaves * RPS;
@@ -140,7 +152,8 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
         const int j = k / QB, r = k % QB;
         const int i = base + first + j * kStride;
         if (i < n && qb + r < nq)
-          store_shared(scores + static_cast<size_t>(row0 + qb + r) * NS + col_of(i), d);
+          store_shared_i32(scores + static_cast<size_t>(row0 + qb + r) * NS + col_of(i),
+                           score_word(d));
       }
     }
   }
@@ -231,15 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   __shared__ bool s_ok;
   const int bid = static_cast<int>(blockIdx.x);
   const int U = ra.B * ra.Hkv;
-  if (bid < U * st.items) {
-    const int u = bid % U, m = bid / U;
-    score_item<T, D>(ra, st, u, m);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // scores performed before the flag
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(st.flags + u * st.items + m, 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (bid < U * st.items) score_item<T, D>(ra, st, bid % U, bid / U);
   const int rows = ra.B * ra.Hq * ra.Nq;
   if (bid >= rows * st.n_splits) return;
 
@@ -247,29 +252,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   const int row = bid / st.n_splits;
   const int split = bid % st.n_splits;
   const int i = row % ra.Nq;
-  const int bh = row / ra.Nq;
-  const int h = bh % ra.Hq;
-  const int b = bh / ra.Hq;
-  const int u = b * ra.Hkv + h / (ra.Hq / ra.Hkv);
-  const int p = route_seq_len(ra, b) - ra.Nq + i;
-  unsigned* flags = st.flags + u * st.items;
-  if (threadIdx.x < kWave) {
-    // wave 0 polls the unit's flags, one word per lane per load
-    bool ok = false;
-    for (int it = 0; it < (1 << 20); ++it) {
-      bool all = true;
-      for (int m = static_cast<int>(threadIdx.x); m < st.items; m += kWave)
-        all = all && __hip_atomic_load(flags + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-      if (__builtin_amdgcn_ballot_w64(!all) == 0) {
-        ok = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (threadIdx.x == 0) s_ok = ok;
-  }
-  __syncthreads();
-  const bool ok = s_ok;
+  const int b = row / ra.Nq / ra.Hq;
+  const int Tb = route_seq_len(ra, b);
+  const int p = Tb - ra.Nq + i;
+  const int NS = ra.n_c + ra.n_g;
+  int32_t* words = st.scores + static_cast<size_t>(row) * NS;
 
   const int cap = kept_capacity(ra);
   float* s_cs = s_dyn;               // chunk scores [n_c]
@@ -281,26 +268,48 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int L = p >= 0 ? p / ra.C : -1;
-  if (p >= 0 && ok) {
-    // the row's scores: chunks 0..L, groups 0..p/G, all loads in flight
-    const int n1 = L + 1;
-    const int n2 = min(ra.n_g, p / ra.G + 1);
-    const float* src = st.scores + static_cast<size_t>(row) * (ra.n_c + ra.n_g);
+  if (threadIdx.x == 0) s_ok = true;
+  __syncthreads();
+  if (Tb > 0) {
+    // Every word the scoring writes for the row (a superset of chunks 0..L and
+    // groups 0..p/G, so that each word is known to have landed before it is
+    // zeroed again). Every thread loads its words with all loads in flight and
+    // reloads the ones still zero (not written yet) until none is (bounded:
+    // the row is poisoned if not).
+    int n1, n2;
+    written_range(ra, Tb, n1, n2);
+    bool ok = true;
     for (int base = 0; base < n1 + n2; base += 8 * kThreads) {
-      float v[8];
+      int32_t v[8];
+      unsigned pending = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
-        v[k] = idx < n1 + n2 ? load_shared(src + (idx < n1 ? idx : ra.n_c + idx - n1)) : 0.f;
+        v[k] = 1;
+        if (idx < n1 + n2) v[k] = load_shared_i32(words + (idx < n1 ? idx : ra.n_c + idx - n1));
+        pending |= static_cast<unsigned>(v[k] == 0) << k;
       }
+      for (int it = 0; pending != 0u && it < (1 << 20); ++it) {
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
+          if ((pending >> k) & 1u) v[k] = load_shared_i32(words + (idx < n1 ? idx : ra.n_c + idx - n1));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pending &= ~(static_cast<unsigned>(v[k] != 0) << k);
+      }
+      ok = ok && pending == 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
-        if (idx < n1 + n2) s_dyn[idx < n1 ? idx : ra.n_c + idx - n1] = v[k];
+        if (idx < n1 + n2) s_dyn[idx < n1 ? idx : ra.n_c + idx - n1] = score_of_word(v[k]);
       }
     }
+    if (!ok) s_ok = false;
   }
   __syncthreads();
+  const bool ok = s_ok;
   if (wave == 0) {
     int n_kept = 0;
     int got = 0;
@@ -348,25 +357,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     }
   }
   __syncthreads();
-  const bool wrote = attend_body<T, D, false, kWaves, true>(aa, st.groups_per_wave, st.n_splits, 0,
-                                                            bid, nullptr, s_ids, !ok);
-  // The row is done: count it in; the unit's last row clears the unit's flags
-  // and counter (never after a timeout, whose outputs are NaN).
-  if (wrote && ok) {
-    const int rpu = (ra.Hq / ra.Hkv) * ra.Nq;
-    if (threadIdx.x == 0) {
-      const unsigned prev =
-          __hip_atomic_fetch_add(st.done + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ok = prev == static_cast<unsigned>(rpu) - 1;
-    }
-    __syncthreads();
-    if (s_ok) {
-      for (int m = static_cast<int>(threadIdx.x); m < st.items; m += kThreads)
-        __hip_atomic_store(flags + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (threadIdx.x == 0)
-        __hip_atomic_store(st.done + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  // Every split of the row has read the row's scores once all have counted
+  // themselves in: the finishing workgroup then zeroes every word the scoring
+  // wrote for the row (each one it saw arrive).
+  auto zero_row = [&]() {
+    if (Tb <= 0) return;
+    int n_chunks, n_groups;
+    written_range(ra, Tb, n_chunks, n_groups);
+    for (int t = static_cast<int>(threadIdx.x); t < n_chunks + n_groups; t += kThreads)
+      store_shared_i32(words + (t < n_chunks ? t : ra.n_c + t - n_chunks), 0);
+  };
+  attend_body<T, D, false, kWaves, true>(aa, st.groups_per_wave, st.n_splits, 0, bid, nullptr,
+                                         s_ids, !ok, zero_row);
 }
 
 // Scoring items per unit: as many as the grid holds (at least two: the refresh
@@ -436,7 +438,7 @@ AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g) {
   pl.groups_per_wave = gpw;
   pl.n_splits = (k_g + W * gpw - 1) / (W * gpw);
   pl.off_counters = 0;
-  pl.off_partials = kCounterBytes;
+  pl.off_partials = kZeroBytes;
   const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;
   pl.bytes = (pl.off_partials + part + 255) / 256 * 256;
   return pl;
@@ -448,30 +450,24 @@ bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int6
   const int64_t rows = B * Hq * Nq, units = B * Hkv;
   if (2 * units > cus) return false;
   if (Nq > C || C / G > rowroute::kFreshMaxGpc) return false;  // the refresh's LDS rows
-  if (units * step_items(units) > kUnitDone) return false;      // the flag words
   const AttendPlan plan = plan_decode_attend(rows, D, k_g);
   if (rows * plan.n_splits > cus) return false;
   const int64_t n_c = (T + C - 1) / C, n_g = (T + G - 1) / G;
+  // the score words live in the workspace's zero-at-rest region
+  if (static_cast<size_t>(rows * (n_c + n_g)) * 4 > kZeroBytes - kCounterBytes) return false;
   const int64_t cap = std::min<int64_t>(k_c + 2, n_c);
   const size_t lds = static_cast<size_t>(n_c + n_g + cap + cap * (C / G) + std::max(k_c, k_g) + k_g) * 4;
   return lds + step_static_lds(D) <= 160 * 1024;
 }
 
-size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t T, int64_t D, int C, int G,
-                         int k_g) {
-  const int64_t rows = B * Hq * Nq;
-  const AttendPlan plan = plan_decode_attend(rows, D, k_g);
-  const size_t scores = static_cast<size_t>(rows * ((T + C - 1) / C + (T + G - 1) / G)) * 4;
-  return (plan.bytes + scores + 255) / 256 * 256;
+size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int k_g) {
+  return plan_decode_attend(B * Hq * Nq, D, k_g).bytes;
 }
 
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
                               int dtype, void* workspace, hipStream_t stream) {
   StepArgs st{};
-  unsigned* words = static_cast<unsigned*>(workspace);
-  st.flags = words + kUnitFlags;
-  st.done = words + kUnitDone;
-  st.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.bytes);
+  st.scores = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kCounterBytes);
   st.items = step_items(static_cast<int64_t>(ra.B) * ra.Hkv);
   st.n_splits = plan.n_splits;
   st.groups_per_wave = plan.groups_per_wave;

@@ -43,6 +43,10 @@ __device__ __forceinline__ bool wait_ready(const unsigned* flag, bool* s_ok) {
   return *s_ok;
 }
 
+struct NoRowHook {
+  __device__ void operator()() const {}
+};
+
 // One attention workgroup: row `row_base + bid / n_splits`, split
 // `bid % n_splits`. With `ready` set (routing and attention in one launch), it
 // first waits until the row's routing workgroup has published the row's group
@@ -50,11 +54,16 @@ __device__ __forceinline__ bool wait_ready(const unsigned* flag, bool* s_ok) {
 // clears the flag again. With LDS_IDS the row's group ids are already in LDS
 // (s_ids, k_group entries), chosen by this workgroup itself; `poisoned` then
 // marks a row whose routing could not be completed (its outputs become NaN).
+// `row_done` is called by every thread of the workgroup that finishes the row,
+// as soon as every split of the row has counted itself in (so every split is
+// past everything it did before its partial sums).
 // Returns true in the workgroup that wrote the row's outputs (its last split).
-template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves, bool LDS_IDS = false>
+template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves, bool LDS_IDS = false,
+          typename RowHook = NoRowHook>
 __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_wave, int n_splits,
                                             int row_base, int bid, unsigned* ready,
-                                            const int* s_ids = nullptr, bool poisoned = false) {
+                                            const int* s_ids = nullptr, bool poisoned = false,
+                                            RowHook row_done = RowHook{}) {
   constexpr int kBodyThreads = WAVES * kWave;
   constexpr int EPL = Elem<TKV>::kPer16;
   constexpr int LPR = D / EPL;        // lanes per token row
@@ -276,6 +285,7 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
   };
 
   if (n_splits == 1) {
+    row_done();
     finish(M, Lsum, acc);
     return true;
   }
@@ -287,6 +297,7 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
   }
   if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
     return false;
+  row_done();
 
   // Pull every split's (m, l, o) into LDS with all loads in flight at once.
   const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);

@@ -11,11 +11,14 @@ namespace hga {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
-// Every workspace starts with this many bytes of arrival counters. Nothing else
-// is ever stored there and every call leaves them at zero, so one workspace can
-// serve calls of any shape in turn. A launch uses at most kMaxCounters of them.
+// Every workspace starts with kZeroBytes that are zero at rest: every call
+// leaves them at zero, so one workspace can serve calls of any shape in turn.
+// The first kCounterBytes hold arrival counters (a launch uses at most
+// kMaxCounters of them); the rest carries the one-launch decode step's
+// hand-off words. Plans put their data after kZeroBytes.
 constexpr size_t kCounterBytes = 65536;
 constexpr int kMaxCounters = static_cast<int>(kCounterBytes / sizeof(unsigned));
+constexpr size_t kZeroBytes = size_t{4} << 20;
 
 // Largest number of items one wave selects from (middle chunks, or candidate
 // groups of the kept chunks), and of chunks one query keeps.
@@ -143,18 +146,19 @@ hipError_t launch_attend_tiles(const AttendArgs& a, hipStream_t stream);
 // Decode step (refresh + score + select + attend) as one launch, every
 // workgroup resident at once (at most one per CU): each scores a slice of one
 // (sequence, KV head)'s summaries for all its query rows, then selects and
-// attends for one (row, split). The workspace holds the attention plan's
-// counters and partials (plan.bytes), then the scores [rows, n_c + n_g].
+// attends for one (row, split). The scores [rows, n_c + n_g] travel as words
+// in the workspace's zero-at-rest region after the counters; the attention
+// plan's counters and partials are as usual (plan.bytes).
 // Attention plan inside the one-launch decode step (8 waves per workgroup).
 AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g);
 // Whether the one-launch form applies: the grid fits one workgroup per CU,
-// the refresh touches at most two chunks of at most 16 groups, and the row's
-// scores and selection fit the LDS.
+// the refresh touches at most two chunks of at most 16 groups, the rows'
+// score words fit the zero-at-rest region, and the row's scores and selection
+// fit the LDS.
 bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int64_t D,
                             int C, int G, int k_c, int k_g);
 // Workspace bytes of the one-launch form.
-size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t T, int64_t D, int C, int G,
-                         int k_g);
+size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int k_g);
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
                               int dtype, void* workspace, hipStream_t stream);
 

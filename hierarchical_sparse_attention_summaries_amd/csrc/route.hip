@@ -225,7 +225,7 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   pl.n_splits = static_cast<int>((n_c + pl.chunks_per_split - 1) / pl.chunks_per_split);
   const int64_t rows = B * Hq * Nq;
   pl.off_counters = 0;
-  pl.off_chunk_scores = kCounterBytes;
+  pl.off_chunk_scores = kZeroBytes;
   pl.off_group_scores = align_up(pl.off_chunk_scores + static_cast<size_t>(rows * n_c) * 4, 256);
   pl.bytes = align_up(pl.off_group_scores + static_cast<size_t>(rows * n_g) * 4, 256);
   pl.off_split = 0;

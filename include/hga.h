@@ -31,11 +31,12 @@
  *     launch failed; faults inside kernels surface at the caller's next
  *     synchronisation, as usual for HIP. Nothing throws, prints or aborts.
  *   - Inputs must be finite (no NaN/Inf in Q, K, V).
- *   - Workspaces: the first 64 KiB of a workspace hold arrival counters and must
- *     be zero before the workspace's first use (e.g. allocate it zeroed). The
- *     library stores nothing else there and every call leaves them at zero, so
- *     one workspace (large enough for each call) can serve calls of any shape
- *     in turn. Calls that may run concurrently must not share a workspace.
+ *   - Workspaces: the first hga_workspace_zero_bytes() bytes (4 MiB) of a
+ *     workspace hold arrival counters and hand-off words and must be zero
+ *     before the workspace's first use (e.g. allocate it zeroed). Every call
+ *     leaves them at zero, so one workspace (large enough for each call) can
+ *     serve calls of any shape in turn. Calls that may run concurrently must
+ *     not share a workspace.
  */
 #ifndef HGA_H
 #define HGA_H
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 1
+#define HGA_ABI_VERSION 2
 
 typedef enum hga_status {
   HGA_OK = 0,
@@ -78,6 +79,10 @@ typedef struct hga_shape {
 
 /* Version of this interface (HGA_ABI_VERSION of the built library). */
 int hga_abi_version(void);
+
+/* Size of the zero-at-rest region every workspace begins with (every
+ * workspace size query below includes it). */
+size_t hga_workspace_zero_bytes(void);
 
 /* Static English text for a status code; never NULL. */
 const char* hga_status_str(int status);
@@ -256,7 +261,7 @@ int hga_attend_staged_sizes(const hga_shape* shape, int32_t group, int32_t k_gro
  *   K_pool, V_pool: device memory of pool_pages pages of [group, D] elements
  *             of `dtype` each, pool_pages >= the count hga_attend_staged_sizes
  *             gives (B*Hkv*min(ceil(T/group), r*Nq*k_group)); scratch.
- *   workspace: hga_attend_staged_sizes bytes; first 64 KiB zero, as always.
+ *   workspace: hga_attend_staged_sizes bytes; its zero region zero, as always.
  * The bytes read from K and V are the distinct routed groups' (what
  * crosses the host link), not every row's.
  */
@@ -267,7 +272,7 @@ int hga_attend_staged(const hga_shape* shape, const void* Q, const void* K, cons
                       void* stream);
 
 /* Workspace bytes hga_decode_step_ex needs. As for every call here, the
- * workspace's first 64 KiB must be zero before its first use and are left
+ * workspace's zero region must be zero before its first use and is left
  * zero; the rest is scratch. */
 int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
                                    int32_t k_chunk, int32_t k_group, size_t* bytes);
@@ -289,15 +294,17 @@ int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t ch
  *   sequence's newest Nq keys are recomputed from K and written;
  *   chunk_idx (or NULL), group_idx, O, lse (or NULL): written as by
  *   hga_route_ex and hga_attend_ex.
- * For small batches (hga_decode_step_one_launch: where hga_route_fresh_ex is
- * one launch and every workgroup of the step fits the device at once, one per
- * CU) the call is one launch: routing workgroups publish each row's group ids
- * and a per-row flag in the workspace; attention workgroups of the same
- * launch wait for the flag (a bounded wait; a row whose routing it does not
- * see in time gets NaN in O and lse, and the workspace's first 64 KiB must
- * then be zeroed before its next use) and the last one of each row clears
- * it. Otherwise the two calls are enqueued. Calls that share a workspace must
- * not overlap.
+ * For small batches (hga_decode_step_one_launch: every workgroup of the step
+ * fits the device at once, one per CU, and the rows' scores fit the
+ * workspace's zero region) the call is one launch: every workgroup scores a
+ * share of one KV head's summaries against all of its query rows and writes
+ * the scores into the zero region as words that are never zero; then it polls
+ * its own row's words until all have arrived (a bounded wait; a row whose
+ * scores do not all arrive in time gets NaN in O and lse, and the zero region
+ * must then be zeroed again before the workspace's next use), selects, and
+ * attends to its share of the row's groups. The workgroup that finishes a row
+ * zeroes the row's words. Otherwise the two calls are enqueued. Calls that
+ * share a workspace must not overlap.
  */
 int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
                        const void* K, const void* V, int32_t dtype, float* chunk_mean,

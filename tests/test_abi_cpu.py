@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_text():
     L = hga.lib()
-    assert L.hga_abi_version() == 1
+    assert L.hga_abi_version() == 2
+    assert hga.WORKSPACE_ZERO_BYTES == 4 << 20
     for s in (OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED, 123):
         assert len(L.hga_status_str(s)) > 0
 

@@ -466,6 +466,14 @@ def _same_attention(O_a, lse_a, O_b, lse_b, dtype):
     assert float((lse_a - lse_b).abs().max()) <= 1e-4
 
 
+def _zero_regions_are_zero():
+    """Every workspace the binding keeps has its zero region back at zero."""
+    Z = hga.WORKSPACE_ZERO_BYTES
+    for key, buf in hga._ws.items():
+        if key[1] in ("route", "attend", "decode", "staged"):   # not the staging pools
+            assert int(buf[:Z].count_nonzero()) == 0, key
+
+
 DECODE_CASES = {
     "bf16-b2-t8192-nq2": DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2),
     "f32-b1-t4096": DECODE_64K.with_(B=1, T=4096, k_chunk=3, k_group=12, plants=1, dtype="f32"),
@@ -504,6 +512,7 @@ def test_decode_step_equals_fresh_route_then_attend(case):
     torch.cuda.synchronize()
     assert torch.equal(g_d, g_r) and torch.equal(c_d, c_r)
     assert torch.equal(cm_d, cm_r) and torch.equal(gm_d, gm_r)
+    _zero_regions_are_zero()
     _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
     if layout is None and w.T <= 8192:
         from synth.inputs import Inputs
@@ -513,8 +522,8 @@ def test_decode_step_equals_fresh_route_then_attend(case):
 
 def test_decode_step_back_to_back_leaves_counters_zero():
     """Successive one-launch decode steps on one workspace (each step's queries
-    differ; only its counters are zero at the start) each match the two-call
-    result, and leave the counters at zero."""
+    differ; only its zero region is zero at the start) each match the two-call
+    result, and leave the zero region (counters and score words) at zero."""
     log("case decode-step back-to-back")
     # two attention workgroups per row, so the arrival counters are used too
     w = DECODE_64K.with_(B=2, T=16384, k_chunk=8, k_group=64, plants=2)
@@ -525,17 +534,20 @@ def test_decode_step_back_to_back_leaves_counters_zero():
     nbytes = hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk, w.k_group)
     # a workspace that an earlier call of another shape left dirty past its counters
     ws = torch.full((nbytes + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
-    ws[:65536] = 0
+    Z = hga.WORKSPACE_ZERO_BYTES
+    ws[:Z] = 0
     for step in range(4):
         Qs = (Q.float() * (1.0 + 0.25 * step)).to(Q.dtype) if step % 2 else Q.flip(1).contiguous()
         O_d, lse_d, _, g_d = hga.decode_step_ex(Qs, K, V, cm, gm, w.T, w.chunk, w.group,
                                                 w.k_chunk, w.k_group, workspace=ws)
-        _, g_r = hga.route_fresh_ex(Qs, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
-        O_r, lse_r = hga.attend(Qs, K, V, g_r, w.group)
+        # the two-call form on the same workspace: it must leave the zero region alone
+        _, g_r = hga.route_fresh_ex(Qs, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                                    workspace=ws)
+        O_r, lse_r = hga.attend(Qs, K, V, g_r, w.group, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(g_d, g_r), step
         _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
-        assert int(ws[:65536].count_nonzero()) == 0
+        assert int(ws[:Z].count_nonzero()) == 0
 
 
 def test_prefill_ragged_with_queries_before_the_first_key():
