@@ -140,10 +140,6 @@ bool row_fresh_fused(const hga_shape* s, int32_t dtype, int32_t chunk, int32_t g
            hga::use_prefill_route(dtype, s->q_heads, s->kv_heads, s->n_queries, s->head_dim));
 }
 
-// Counter words of the one-launch decode step: the attention's split counters
-// sit at [kDecodeAttendCounters, +rows) (rows <= the CU count there).
-constexpr int kDecodeAttendCounters = 0;
-
 // Whether hga_decode_step_ex runs as one launch (small batches).
 bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
                        int32_t k_group) {
@@ -153,8 +149,8 @@ bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t
 
 // Workspace of hga_decode_step_ex: the larger of the two-call form (routing,
 // then attention in stream order over the same workspace) and the one-launch
-// form (the attention's counters and partials; the rows' score words sit in
-// the zero-at-rest region every workspace begins with).
+// form (its score and partial words sit in the zero-at-rest region every
+// workspace begins with).
 size_t decode_workspace_bytes(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
                               int32_t k_group) {
   const int64_t rows = s->batch * s->q_heads * s->n_queries;
@@ -591,7 +587,6 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   ra.kv = L;
   hga::AttendArgs aa = attend_args(shape, L, Q, K, V, group_idx, k_group, group, scale, O, lse,
                                    ws, aplan);
-  aa.counters = reinterpret_cast<unsigned*>(ws) + kDecodeAttendCounters;
   const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ws, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }

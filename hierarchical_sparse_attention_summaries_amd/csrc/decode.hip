@@ -12,7 +12,7 @@
 // recomputes the chunks holding the sequence's newest keys from K (same bits
 // as the summaries kernel), writes them out and scores them; the others split
 // the older summaries evenly. Scores go to the workspace's zero-at-rest region
-// with agent-coherent stores, as words that are never zero (score_word), so a
+// with agent-coherent stores, as words that are never zero (handoff_word), so a
 // score that has arrived is its own ready signal: no flag, no wait for the
 // stores to be acknowledged, no second read. Scoring never waits.
 //
@@ -23,7 +23,9 @@
 // share of the routed keys and values. Split 0 writes the row's ids out. The
 // workgroup that finishes a row (every split has counted itself in, so every
 // split has read the row's scores) zeroes the row's score words for the next
-// call.
+// call. The splits' partial sums go the same way: splits 1.. leave them as
+// hand-off words in the zero-at-rest region and split 0 polls, merges and
+// zeroes them, so the step uses no counter at all.
 //
 // Against one workgroup per query row running both levels back to back, this
 // reads every group summary (not only the candidates'), spread over every CU,
@@ -44,16 +46,6 @@ struct StepArgs {
   int n_splits;       // attention workgroups per row
   int groups_per_wave;
 };
-
-// A score as a workspace word: the bits of s + 0 (so never -0) with the sign
-// bit flipped, which is never zero; zero marks a score not written yet. The
-// round trip gives s, or +0 for -0, which has the same selection key.
-__device__ __forceinline__ int32_t score_word(float s) {
-  return __float_as_int(s + 0.0f) ^ static_cast<int32_t>(0x80000000u);
-}
-__device__ __forceinline__ float score_of_word(int32_t w) {
-  return __int_as_float(w ^ static_cast<int32_t>(0x80000000u));
-}
 
 // Score words a scoring pass writes for each query row of a unit whose
 // sequence holds Tb > 0 keys: chunks [0, n_chunks), groups [0, n_groups).
@@ -153,7 +145,7 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
         const int i = base + first + j * kStride;
         if (i < n && qb + r < nq)
           store_shared_i32(scores + static_cast<size_t>(row0 + qb + r) * NS + col_of(i),
-                           score_word(d));
+                           handoff_word(d));
       }
     }
   }
@@ -303,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
-        if (idx < n1 + n2) s_dyn[idx < n1 ? idx : ra.n_c + idx - n1] = score_of_word(v[k]);
+        if (idx < n1 + n2) s_dyn[idx < n1 ? idx : ra.n_c + idx - n1] = handoff_float(v[k]);
       }
     }
     if (!ok) s_ok = false;
@@ -367,8 +359,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     for (int t = static_cast<int>(threadIdx.x); t < n_chunks + n_groups; t += kThreads)
       store_shared_i32(words + (t < n_chunks ? t : ra.n_c + t - n_chunks), 0);
   };
-  attend_body<T, D, false, kWaves, true>(aa, st.groups_per_wave, st.n_splits, 0, bid, nullptr,
-                                         s_ids, !ok, zero_row);
+  attend_body<T, D, false, kWaves, true, decltype(zero_row), true>(
+      aa, st.groups_per_wave, st.n_splits, 0, bid, nullptr, s_ids, !ok, zero_row);
 }
 
 // Scoring items per unit: as many as the grid holds (at least two: the refresh
@@ -425,6 +417,19 @@ size_t step_static_lds(int64_t D) {
 
 }  // namespace
 
+// Where the step's hand-off words sit in the zero-at-rest region: the rows'
+// score words after the counters, then the splits' partials.
+struct StepWords {
+  size_t scores, partials, end;
+};
+static StepWords step_words(int64_t rows, int64_t NS, int n_splits, int64_t D) {
+  StepWords w{};
+  w.scores = kCounterBytes;
+  w.partials = (w.scores + static_cast<size_t>(rows * NS) * 4 + 255) / 256 * 256;
+  w.end = w.partials + (n_splits > 1 ? static_cast<size_t>(rows * n_splits * (D + 2)) * 4 : 0);
+  return w;
+}
+
 AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g) {
   // The fewest groups per wave (8 waves per workgroup) that keep one
   // workgroup per (row, split) within one per CU.
@@ -437,10 +442,10 @@ AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g) {
   AttendPlan pl{};
   pl.groups_per_wave = gpw;
   pl.n_splits = (k_g + W * gpw - 1) / (W * gpw);
+  // the partials are hand-off words in the zero-at-rest region (step_words)
   pl.off_counters = 0;
-  pl.off_partials = kZeroBytes;
-  const size_t part = pl.n_splits > 1 ? static_cast<size_t>(rows) * pl.n_splits * (D + 2) * 4 : 0;
-  pl.bytes = (pl.off_partials + part + 255) / 256 * 256;
+  pl.off_partials = 0;
+  pl.bytes = kZeroBytes;
   return pl;
 }
 
@@ -453,8 +458,8 @@ bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int6
   const AttendPlan plan = plan_decode_attend(rows, D, k_g);
   if (rows * plan.n_splits > cus) return false;
   const int64_t n_c = (T + C - 1) / C, n_g = (T + G - 1) / G;
-  // the score words live in the workspace's zero-at-rest region
-  if (static_cast<size_t>(rows * (n_c + n_g)) * 4 > kZeroBytes - kCounterBytes) return false;
+  // the score and partial words live in the workspace's zero-at-rest region
+  if (step_words(rows, n_c + n_g, plan.n_splits, D).end > kZeroBytes) return false;
   const int64_t cap = std::min<int64_t>(k_c + 2, n_c);
   const size_t lds = static_cast<size_t>(n_c + n_g + cap + cap * (C / G) + std::max(k_c, k_g) + k_g) * 4;
   return lds + step_static_lds(D) <= 160 * 1024;
@@ -466,16 +471,21 @@ size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int k_g) 
 
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
                               int dtype, void* workspace, hipStream_t stream) {
+  const StepWords w = step_words(static_cast<int64_t>(ra.B) * ra.Hq * ra.Nq, ra.n_c + ra.n_g,
+                                 plan.n_splits, ra.D);
+  char* ws = static_cast<char*>(workspace);
   StepArgs st{};
-  st.scores = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kCounterBytes);
+  st.scores = reinterpret_cast<int32_t*>(ws + w.scores);
+  AttendArgs a2 = aa;
+  a2.partials = reinterpret_cast<float*>(ws + w.partials);
   st.items = step_items(static_cast<int64_t>(ra.B) * ra.Hkv);
   st.n_splits = plan.n_splits;
   st.groups_per_wave = plan.groups_per_wave;
   if (dtype == kF32)
-    return ra.D == 64 ? launch_td<float, 64>(ra, aa, st, stream)
-                      : launch_td<float, 128>(ra, aa, st, stream);
-  return ra.D == 64 ? launch_td<uint16_t, 64>(ra, aa, st, stream)
-                    : launch_td<uint16_t, 128>(ra, aa, st, stream);
+    return ra.D == 64 ? launch_td<float, 64>(ra, a2, st, stream)
+                      : launch_td<float, 128>(ra, a2, st, stream);
+  return ra.D == 64 ? launch_td<uint16_t, 64>(ra, a2, st, stream)
+                    : launch_td<uint16_t, 128>(ra, a2, st, stream);
 }
 
 }  // namespace hga

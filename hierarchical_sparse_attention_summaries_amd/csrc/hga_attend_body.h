@@ -57,9 +57,13 @@ struct NoRowHook {
 // `row_done` is called by every thread of the workgroup that finishes the row,
 // as soon as every split of the row has counted itself in (so every split is
 // past everything it did before its partial sums).
-// Returns true in the workgroup that wrote the row's outputs (its last split).
+// With POLL_MERGE (every workgroup of the row resident at once), the partials
+// go to memory that is zero at rest as hand-off words instead: splits 1.. store
+// theirs and are done, and split 0 polls them (bounded; NaN outputs if one
+// does not arrive in time), merges, and zeroes them again; no counters.
+// Returns true in the workgroup that wrote the row's outputs.
 template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves, bool LDS_IDS = false,
-          typename RowHook = NoRowHook>
+          typename RowHook = NoRowHook, bool POLL_MERGE = false>
 __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_wave, int n_splits,
                                             int row_base, int bid, unsigned* ready,
                                             const int* s_ids = nullptr, bool poisoned = false,
@@ -239,6 +243,7 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     s_m[wave] = m;
     s_l[wave] = l;
   }
+  if (threadIdx.x == 0) s_last = true;
   if (sub == 0) {
 #pragma unroll
     for (int k = 0; k < EPL; ++k) s_o[wave][col + k] = o[k];
@@ -289,33 +294,88 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     finish(M, Lsum, acc);
     return true;
   }
-  float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
-  if (d < D) store_shared(part + 2 + d, acc);
-  if (d == 0) {
-    store_shared(part, M);
-    store_shared(part + 1, Lsum);
-  }
-  if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
-    return false;
-  row_done();
+  if constexpr (POLL_MERGE) {
+    int32_t* slots = reinterpret_cast<int32_t*>(a.partials) +
+                     static_cast<size_t>(row) * n_splits * (D + 2);
+    if (split != 0) {
+      int32_t* mine = slots + split * (D + 2);
+      if (d < D) store_shared_i32(mine + 2 + d, handoff_word(acc));
+      if (d == 0) {
+        store_shared_i32(mine, handoff_word(M));
+        store_shared_i32(mine + 1, handoff_word(Lsum));
+      }
+      return false;
+    }
+    // split 0: its own partial goes to slot 0 in LDS, the others' as they land
+    if (d < D) s_part[2 + d] = acc;
+    if (d == 0) {
+      s_part[0] = M;
+      s_part[1] = Lsum;
+    }
+    const int total = (n_splits - 1) * (D + 2);
+    bool arrived = true;
+    for (int base = 0; base < total; base += 4 * kBodyThreads) {
+      int32_t v[4];
+      unsigned pending = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * kBodyThreads + threadIdx.x;
+        v[u] = idx < total ? load_shared_i32(slots + D + 2 + idx) : 1;
+        pending |= static_cast<unsigned>(v[u] == 0) << u;
+      }
+      for (int it = 0; pending != 0u && it < (1 << 20); ++it) {
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = base + u * kBodyThreads + threadIdx.x;
+          if ((pending >> u) & 1u) v[u] = load_shared_i32(slots + D + 2 + idx);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pending &= ~(static_cast<unsigned>(v[u] != 0) << u);
+      }
+      arrived = arrived && pending == 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * kBodyThreads + threadIdx.x;
+        if (idx < total) s_part[D + 2 + idx] = handoff_float(v[u]);
+      }
+    }
+    if (!arrived) s_last = false;
+    __syncthreads();
+    if (!s_last) timed_out = true;
+    // every other split has stored its partial, so is past the row's scores
+    row_done();
+    for (int idx = threadIdx.x; idx < total; idx += kBodyThreads)
+      store_shared_i32(slots + D + 2 + idx, 0);
+  } else {
+    float* part = a.partials + (static_cast<size_t>(row) * n_splits + split) * (D + 2);
+    if (d < D) store_shared(part + 2 + d, acc);
+    if (d == 0) {
+      store_shared(part, M);
+      store_shared(part + 1, Lsum);
+    }
+    if (!arrive_last(a.counters + (row - row_base), static_cast<unsigned>(n_splits), &s_last))
+      return false;
+    row_done();
 
-  // Pull every split's (m, l, o) into LDS with all loads in flight at once.
-  const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
-  const int total = n_splits * (D + 2);
-  for (int base = 0; base < total; base += 4 * kBodyThreads) {
-    float v[4];
+    // Pull every split's (m, l, o) into LDS with all loads in flight at once.
+    const float* rp = a.partials + static_cast<size_t>(row) * n_splits * (D + 2);
+    const int total = n_splits * (D + 2);
+    for (int base = 0; base < total; base += 4 * kBodyThreads) {
+      float v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * kBodyThreads + threadIdx.x;
-      v[u] = idx < total ? load_shared(rp + idx) : 0.f;
-    }
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * kBodyThreads + threadIdx.x;
+        v[u] = idx < total ? load_shared(rp + idx) : 0.f;
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * kBodyThreads + threadIdx.x;
-      if (idx < total) s_part[idx] = v[u];
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * kBodyThreads + threadIdx.x;
+        if (idx < total) s_part[idx] = v[u];
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   float Mx = -INFINITY;
   for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, s_part[s * (D + 2)]);
   float Lx = 0.f, ox = 0.f;

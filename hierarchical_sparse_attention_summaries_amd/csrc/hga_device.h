@@ -254,6 +254,17 @@ __device__ __forceinline__ int32_t load_shared_i32(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A float as a hand-off word in memory that is zero at rest: the bits of x + 0
+// (so never -0) with the sign bit flipped, which is never zero, so a reader
+// that sees a non-zero word has the value (no flag needed). The round trip
+// gives x, or +0 for -0.
+__device__ __forceinline__ int32_t handoff_word(float x) {
+  return __float_as_int(x + 0.0f) ^ static_cast<int32_t>(0x80000000u);
+}
+__device__ __forceinline__ float handoff_float(int32_t w) {
+  return __int_as_float(w ^ static_cast<int32_t>(0x80000000u));
+}
+
 // Called by every thread of a workgroup after it issued its store_shared()
 // results. Returns true in exactly one workgroup of the `total` that share
 // `counter`: the last to arrive, which can then read every other workgroup's

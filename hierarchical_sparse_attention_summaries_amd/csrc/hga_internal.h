@@ -146,15 +146,15 @@ hipError_t launch_attend_tiles(const AttendArgs& a, hipStream_t stream);
 // Decode step (refresh + score + select + attend) as one launch, every
 // workgroup resident at once (at most one per CU): each scores a slice of one
 // (sequence, KV head)'s summaries for all its query rows, then selects and
-// attends for one (row, split). The scores [rows, n_c + n_g] travel as words
-// in the workspace's zero-at-rest region after the counters; the attention
-// plan's counters and partials are as usual (plan.bytes).
+// attends for one (row, split). The scores [rows, n_c + n_g] and the splits'
+// partial sums travel as hand-off words in the workspace's zero-at-rest
+// region after the counters; no counter is used.
 // Attention plan inside the one-launch decode step (8 waves per workgroup).
 AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g);
 // Whether the one-launch form applies: the grid fits one workgroup per CU,
-// the refresh touches at most two chunks of at most 16 groups, the rows'
-// score words fit the zero-at-rest region, and the row's scores and selection
-// fit the LDS.
+// the refresh touches at most two chunks of at most 16 groups, the step's
+// hand-off words fit the zero-at-rest region, and the row's scores and
+// selection fit the LDS.
 bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int64_t D,
                             int C, int G, int k_c, int k_g);
 // Workspace bytes of the one-launch form.
