@@ -56,16 +56,79 @@ __device__ __forceinline__ void written_range(const RouteArgs& a, int Tb, int& n
   n_groups = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G);
 }
 
+// The unit's query rows, scaled, for the scoring: with nq <= kPreQ rows they
+// are staged once per workgroup in LDS (thread t holds 8 dims of row
+// t / (D / 8) in flight from q_issue until q_stage writes them), so that every
+// lane reads them instead of loading and converting its own copy.
+constexpr int kPreQ = 16;
+
+template <typename TQ, int D>
+__device__ __forceinline__ void q_issue(const RouteArgs& a, int row0, int nq, uint4& r0,
+                                        uint4& r1) {
+  constexpr int LPQ = D / 8;
+  const int qj = threadIdx.x / LPQ, qcol = (threadIdx.x % LPQ) * 8;
+  r0 = r1 = make_uint4(0, 0, 0, 0);
+  if (qj < nq && qj < kPreQ) {
+    const size_t off = static_cast<size_t>(row0 + qj) * D + qcol;
+    if constexpr (sizeof(TQ) == 4) {
+      r0 = ld16(static_cast<const float*>(a.Q) + off);
+      r1 = ld16(static_cast<const float*>(a.Q) + off + 4);
+    } else {
+      r0 = ld16(static_cast<const uint16_t*>(a.Q) + off);
+    }
+  }
+}
+
+// q = widen(Q) * scale, the values the row route uses.
+template <typename TQ>
+__device__ __forceinline__ void q_scaled(const uint4& r0, const uint4& r1, float scale,
+                                         float (&q)[8]) {
+  if constexpr (sizeof(TQ) == 4) {
+    float x0[4], x1[4];
+    widen(r0, x0);
+    widen(r1, x1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[e] = x0[e] * scale;
+      q[4 + e] = x1[e] * scale;
+    }
+  } else {
+    widen(r0, q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] *= scale;
+  }
+}
+
+template <typename TQ, int D>
+__device__ __forceinline__ void q_stage(const RouteArgs& a, int nq, const uint4& r0,
+                                        const uint4& r1, float (*s_q)[D]) {
+  constexpr int LPQ = D / 8;
+  const int qj = threadIdx.x / LPQ, qcol = (threadIdx.x % LPQ) * 8;
+  if (qj < kPreQ) {  // rows nq.. are zero, so that readers need no bounds test
+    float q[8];
+    q_scaled<TQ>(r0, r1, a.scale, q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_q[qj][qcol + e] = qj < nq ? q[e] : 0.f;
+  }
+}
+
 // Scores summary rows i in [0, n) (row_ptr(i): D floats, all of one pointer
 // kind) against query rows row0 .. row0 + nq - 1: the score of query row j and
 // summary row i goes to scores[(row0 + j) * NS + col_of(i)] as a score word. Lane l of wave w
 // holds dims [(l % LPR) * 8, +8) of summary rows w * RPS + l / LPR + k * kStride;
 // the dot product is the row route's, in the same order, so both give the same
-// bits.
+// bits. Waves without summary rows in a pass skip its arithmetic.
+// Query rows: with s_q given (nq <= kPreQ), from LDS; `stage` then means that
+// this call writes them there from q_issue's registers (r0, r1) once the first
+// pass's summary loads are in flight (a workgroup barrier: every thread of the
+// workgroup calls). Without s_q, every lane loads its rows from Q.
 template <typename TQ, int D, typename RowPtr, typename ColOf>
 __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq, int n,
                                             RowPtr row_ptr, ColOf col_of, int32_t* scores,
-                                            int NS) {
+                                            int NS, float (*s_q)[D] = nullptr,
+                                            bool stage = false,
+                                            const uint4& r0 = make_uint4(0, 0, 0, 0),
+                                            const uint4& r1 = make_uint4(0, 0, 0, 0)) {
   constexpr int LPR = D / 8;
   constexpr int RPS = kWave / LPR;
   constexpr int kStride = kWaves * RPS;
@@ -73,13 +136,15 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
   constexpr int QB = 8;  // query rows per pass
   const int lane = lane_id();
   const int col = (lane % LPR) * 8;
-  const int first = (threadIdx.x / kWave) * RPS + lane / LPR;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int first = wave * RPS + lane / LPR;
   for (int base = 0; base < n; base += NB * kStride) {
+    const bool live = base + wave * RPS < n;  // the wave has rows in this pass
     float4 v0[NB], v1[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int i = base + first + j * kStride;
-      if (i < n) {
+      if (live && i < n) {
         const float* src = row_ptr(i) + col;
         v0[j] = *reinterpret_cast<const float4*>(src);
         v1[j] = *reinterpret_cast<const float4*>(src + 4);
@@ -87,29 +152,44 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
         v0[j] = v1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+    if (stage && base == 0) {
+      q_stage<TQ, D>(a, nq, r0, r1, s_q);
+      __syncthreads();
+    }
+    if (!live) continue;
     for (int qb = 0; qb < nq; qb += QB) {
       float q[QB][8];
+      if (s_q != nullptr) {  // all kPreQ rows are written (zero past nq)
 #pragma unroll
-      for (int r = 0; r < QB; ++r) {
-        if (qb + r < nq) {
-          const size_t off = static_cast<size_t>(row0 + qb + r) * D + col;
-          if constexpr (sizeof(TQ) == 4) {
-            float x0[4], x1[4];
-            widen(ld16(static_cast<const float*>(a.Q) + off), x0);
-            widen(ld16(static_cast<const float*>(a.Q) + off + 4), x1);
+        for (int r = 0; r < QB; ++r) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&s_q[qb + r][col]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&s_q[qb + r][col + 4]);
+          q[r][0] = x0.x; q[r][1] = x0.y; q[r][2] = x0.z; q[r][3] = x0.w;
+          q[r][4] = x1.x; q[r][5] = x1.y; q[r][6] = x1.z; q[r][7] = x1.w;
+        }
+      } else {
+        // all of the pass's query loads in flight at once
+        uint4 raw0[QB], raw1[QB];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              q[r][e] = x0[e] * a.scale;
-              q[r][4 + e] = x1[e] * a.scale;
+        for (int r = 0; r < QB; ++r) {
+          raw0[r] = raw1[r] = make_uint4(0, 0, 0, 0);
+          if (qb + r < nq) {
+            const size_t off = static_cast<size_t>(row0 + qb + r) * D + col;
+            if constexpr (sizeof(TQ) == 4) {
+              raw0[r] = ld16(static_cast<const float*>(a.Q) + off);
+              raw1[r] = ld16(static_cast<const float*>(a.Q) + off + 4);
+            } else {
+              raw0[r] = ld16(static_cast<const uint16_t*>(a.Q) + off);
             }
-          } else {
-            widen(ld16(static_cast<const uint16_t*>(a.Q) + off), q[r]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) q[r][e] *= a.scale;
           }
-        } else {
+        }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[r][e] = 0.f;
+        for (int r = 0; r < QB; ++r) {
+          q_scaled<TQ>(raw0[r], raw1[r], a.scale, q[r]);
+          if (qb + r >= nq) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[r][e] = 0.f;
+          }
         }
       }
       // partial dot products over this lane's 8 dims, value k = j * QB + r
@@ -151,11 +231,16 @@ __device__ __forceinline__ void score_block(const RouteArgs& a, int row0, int nq
   }
 }
 
-// Scoring item m of unit u (see the top of the file).
+// Refreshed summaries of a unit in LDS: chunk c at row c - cf, group g at row
+// kFreshChunks + g - cf * gpc.
+template <int D>
+using FreshRows = float[rowroute::kFreshChunks * (1 + rowroute::kFreshMaxGpc)][D];
+
+// Scoring item m of unit u (see the top of the file). Item 0 leaves the
+// refreshed summaries in s_fr for write_refreshed.
 template <typename TQ, int D>
-__device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s, int u, int m) {
-  __shared__ float s_fc[rowroute::kFreshChunks][D];
-  __shared__ float s_fg[rowroute::kFreshChunks * rowroute::kFreshMaxGpc][D];
+__device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s, int u, int m,
+                                           FreshRows<D>& s_fr) {
   __shared__ float s_part[kWaves][D];
   const int b = u / a.Hkv;
   const int kv = u % a.Hkv;
@@ -170,36 +255,42 @@ __device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s
   const size_t bkv = static_cast<size_t>(u);
   const float* cm = a.chunk_mean + bkv * a.n_c * D;
   const float* gm = a.group_mean + bkv * a.n_g * D;
+  // The unit's query rows (at most kPreQ) are read first, before anything the
+  // item waits for, and staged in LDS once.
+  __shared__ float s_q[kPreQ][D];
+  const bool pre_q = rpu <= kPreQ;
+  uint4 qr0, qr1;
+  q_issue<TQ, D>(a, row0, pre_q ? rpu : 0, qr0, qr1);
   if (m == 0) {
     constexpr int EPL = Elem<TQ>::kPer16;
-    float* cm_w = const_cast<float*>(cm);
-    float* gm_w = const_cast<float*>(gm);
     for (int c = cf; c <= cl; ++c) {
       chunk_summary<TQ, D, kWaves>(
           static_cast<const TQ*>(a.K), a.kv, b, a.Hkv, kv, a.T, Tb, a.C, a.G, c, s_part,
           [&](int g, int col, const float (&sum)[EPL], int count) {
             const float inv = 1.f / static_cast<float>(count);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-              const float v = sum[e] * inv;
-              gm_w[static_cast<size_t>(g) * D + col + e] = v;
-              s_fg[g - cf * a.gpc][col + e] = v;
-            }
+            for (int e = 0; e < EPL; ++e)
+              s_fr[rowroute::kFreshChunks + g - cf * a.gpc][col + e] = sum[e] * inv;
           },
           [&](int d, float sum, int count) {
-            const float v = sum / static_cast<float>(count);
-            cm_w[static_cast<size_t>(c) * D + d] = v;
-            s_fc[c - cf][d] = v;
+            s_fr[c - cf][d] = sum / static_cast<float>(count);
           });
+      __syncthreads();
+    }
+    if (pre_q) {
+      q_stage<TQ, D>(a, rpu, qr0, qr1, s_q);
       __syncthreads();
     }
     const int nfc = cl - cf + 1;
     const int g0 = cf * a.gpc;
     const int nfg = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G) - g0;
+    // (one LDS base, so that these reads are known to be LDS reads and do not
+    // wait for outstanding global memory operations)
     score_block<TQ, D>(
         a, row0, rpu, nfc + nfg,
-        [&](int i) { return i < nfc ? &s_fc[i][0] : &s_fg[i - nfc][0]; },
-        [&](int i) { return i < nfc ? cf + i : a.n_c + g0 + i - nfc; }, s.scores, NS);
+        [&](int i) { return &s_fr[i < nfc ? i : rowroute::kFreshChunks + i - nfc][0]; },
+        [&](int i) { return i < nfc ? cf + i : a.n_c + g0 + i - nfc; }, s.scores, NS,
+        pre_q ? s_q : nullptr);
   } else {
     // the older summaries: chunks [0, cf), then groups [0, cf * gpc)
     const int n_old = cf * (1 + a.gpc);
@@ -217,7 +308,32 @@ __device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s
             const int j = j0 + i;
             return j < cf ? j : a.n_c + j - cf;
           },
-          s.scores, NS);
+          s.scores, NS, pre_q ? s_q : nullptr, pre_q, qr0, qr1);
+    }
+  }
+}
+
+// Item 0 of unit u, at the end of its workgroup's work: the refreshed
+// summaries go out from LDS (nothing in the launch reads them, so their stores
+// need not hold up the workgroup's attention part).
+template <int D>
+__device__ __forceinline__ void write_refreshed(const RouteArgs& a, int u, const FreshRows<D>& s_fr) {
+  const int b = u / a.Hkv;
+  const int Tb = route_seq_len(a, b);
+  if (Tb <= 0) return;
+  const int cf = max(0, Tb - a.Nq) / a.C;
+  const int cl = (Tb - 1) / a.C;
+  const int nfc = cl - cf + 1;
+  const int g0 = cf * a.gpc;
+  const int nfg = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G) - g0;
+  float* cm_w = const_cast<float*>(a.chunk_mean) + (static_cast<size_t>(u) * a.n_c + cf) * D;
+  float* gm_w = const_cast<float*>(a.group_mean) + (static_cast<size_t>(u) * a.n_g + g0) * D;
+  for (int t = static_cast<int>(threadIdx.x); t < (nfc + nfg) * D; t += kThreads) {
+    const int i = t / D, d = t % D;
+    if (i < nfc) {
+      cm_w[t] = s_fr[i][d];
+    } else {
+      gm_w[t - nfc * D] = s_fr[rowroute::kFreshChunks + i - nfc][d];
     }
   }
 }
@@ -236,9 +352,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   __shared__ bool s_ok;
   const int bid = static_cast<int>(blockIdx.x);
   const int U = ra.B * ra.Hkv;
-  if (bid < U * st.items) score_item<T, D>(ra, st, bid % U, bid / U);
+  __shared__ FreshRows<D> s_fr;
+  if (bid < U * st.items) score_item<T, D>(ra, st, bid % U, bid / U, s_fr);
   const int rows = ra.B * ra.Hq * ra.Nq;
-  if (bid >= rows * st.n_splits) return;
+  if (bid >= rows * st.n_splits) {
+    if (bid < U) write_refreshed<D>(ra, bid, s_fr);
+    return;
+  }
 
   // ---- this workgroup's attention item: row, split
   const int row = bid / st.n_splits;
@@ -260,69 +380,98 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int L = p >= 0 ? p / ra.C : -1;
-  if (threadIdx.x == 0) s_ok = true;
-  __syncthreads();
-  if (Tb > 0) {
-    // Every word the scoring writes for the row (a superset of chunks 0..L and
-    // groups 0..p/G, so that each word is known to have landed before it is
-    // zeroed again). Every thread loads its words with all loads in flight and
-    // reloads the ones still zero (not written yet) until none is (bounded:
-    // the row is poisoned if not).
-    int n1, n2;
-    written_range(ra, Tb, n1, n2);
-    bool ok = true;
-    for (int base = 0; base < n1 + n2; base += 8 * kThreads) {
+  // The row's score words: every word the scoring writes for the row (a
+  // superset of chunks 0..L and groups 0..p/G, so that each word is known to
+  // have landed before it is zeroed again). A polling thread loads its words
+  // with all loads in flight and reloads the ones still zero (not written yet)
+  // until none is (bounded: the row is poisoned if not), decoding them into
+  // LDS. Chunk words [c0, c1) and group words [g0, g1), spread over the nthr
+  // threads numbered tid.
+  auto poll = [&](int c0, int c1, int g0, int g1, int tid, int nthr) {
+    const int nc = c1 - c0, total = nc + g1 - g0;
+    bool arrived = true;
+    for (int base = 0; base < total; base += 8 * nthr) {
       int32_t v[8];
       unsigned pending = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
+        const int idx = base + k * nthr + tid;
         v[k] = 1;
-        if (idx < n1 + n2) v[k] = load_shared_i32(words + (idx < n1 ? idx : ra.n_c + idx - n1));
+        if (idx < total) v[k] = load_shared_i32(words + (idx < nc ? c0 + idx : ra.n_c + g0 + idx - nc));
         pending |= static_cast<unsigned>(v[k] == 0) << k;
       }
       for (int it = 0; pending != 0u && it < (1 << 20); ++it) {
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
-          if ((pending >> k) & 1u) v[k] = load_shared_i32(words + (idx < n1 ? idx : ra.n_c + idx - n1));
+          const int idx = base + k * nthr + tid;
+          if ((pending >> k) & 1u)
+            v[k] = load_shared_i32(words + (idx < nc ? c0 + idx : ra.n_c + g0 + idx - nc));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) pending &= ~(static_cast<unsigned>(v[k] != 0) << k);
       }
-      ok = ok && pending == 0u;
+      arrived = arrived && pending == 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int idx = base + k * kThreads + static_cast<int>(threadIdx.x);
-        if (idx < n1 + n2) s_dyn[idx < n1 ? idx : ra.n_c + idx - n1] = handoff_float(v[k]);
+        const int idx = base + k * nthr + tid;
+        if (idx < total) s_dyn[idx < nc ? c0 + idx : ra.n_c + g0 + idx - nc] = handoff_float(v[k]);
       }
     }
-    if (!ok) s_ok = false;
+    if (!arrived) s_ok = false;
+  };
+  // Level 1 (wave 0): chunk 0, chunk L and the k_chunk best between.
+  auto level1 = [&]() -> int {
+    if (L + 1 <= ra.k_c + 2) {
+      for (int t = lane; t <= L; t += kWave) s_kept[t] = t;
+      wave_lds_sync();
+      return L + 1;
+    }
+    const int gc = ra.k_c > 0 ? rowroute::wave_select<E>(
+                                    L - 1, ra.k_c, [&](int t) { return s_cs[1 + t]; }, s_pick)
+                              : 0;
+    wave_lds_sync();
+    for (int t = lane; t < gc; t += kWave) s_kept[1 + t] = 1 + s_pick[t];
+    if (lane == 0) {
+      s_kept[0] = 0;
+      s_kept[ra.k_c + 1] = L;
+    }
+    wave_lds_sync();
+    return ra.k_c + 2;
+  };
+
+  // The older words come from the other scoring items, the refreshed ones
+  // (chunks cf.., groups cf * gpc..) from item 0, which finishes last. Level 1
+  // needs only chunks 1..L-1, so when those are all older chunks, wave 0
+  // selects them while the other waves wait for the refreshed words.
+  int n1 = 0, n2 = 0, cf = 0;
+  if (Tb > 0) {
+    written_range(ra, Tb, n1, n2);
+    cf = max(0, Tb - ra.Nq) / ra.C;
   }
+  const int gf = min(cf * ra.gpc, n2);
+  const bool early = p >= 0 && L - 1 < cf;
+  if (threadIdx.x == 0) s_ok = true;
   __syncthreads();
+  poll(0, cf, 0, gf, threadIdx.x, kThreads);
+  if (!early) poll(cf, n1, gf, n2, threadIdx.x, kThreads);
+  __syncthreads();
+  int n_kept = 0;
+  if (early) {
+    if (wave == 0) {
+      n_kept = level1();
+    } else {
+      poll(cf, n1, gf, n2, threadIdx.x - kWave, kThreads - kWave);
+    }
+    __syncthreads();
+  } else if (wave == 0 && p >= 0) {
+    n_kept = level1();
+  }
   const bool ok = s_ok;
   if (wave == 0) {
-    int n_kept = 0;
     int got = 0;
+    if (!ok) n_kept = 0;  // a poisoned row routes to nothing
     if (p >= 0 && ok) {
-      // level 1: chunk 0, chunk L and the k_chunk best between
-      if (L + 1 <= ra.k_c + 2) {
-        n_kept = L + 1;
-        for (int t = lane; t < n_kept; t += kWave) s_kept[t] = t;
-      } else {
-        n_kept = ra.k_c + 2;
-        const int gc = ra.k_c > 0 ? rowroute::wave_select<E>(
-                                        L - 1, ra.k_c, [&](int t) { return s_cs[1 + t]; }, s_pick)
-                                  : 0;
-        wave_lds_sync();
-        for (int t = lane; t < gc; t += kWave) s_kept[1 + t] = 1 + s_pick[t];
-        if (lane == 0) {
-          s_kept[0] = 0;
-          s_kept[n_kept - 1] = L;
-        }
-      }
-      wave_lds_sync();
       // level 2: the groups of the kept chunks that start at or before p;
       // invalid candidates sit only at the end of the list (last kept chunk)
       const int n_cand = n_kept * ra.gpc;
@@ -361,6 +510,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   };
   attend_body<T, D, false, kWaves, true, decltype(zero_row), true>(
       aa, st.groups_per_wave, st.n_splits, 0, bid, nullptr, s_ids, !ok, zero_row);
+  if (bid < U) write_refreshed<D>(ra, bid, s_fr);
 }
 
 // Scoring items per unit: as many as the grid holds (at least two: the refresh
@@ -409,8 +559,7 @@ hipError_t launch_td(const RouteArgs& ra, const AttendArgs& aa, const StepArgs& 
 
 // Static LDS of decode_kernel (bound): the refresh's rows and the attention's.
 size_t step_static_lds(int64_t D) {
-  const int fresh_rows = rowroute::kFreshChunks + rowroute::kFreshChunks * rowroute::kFreshMaxGpc +
-                         kWaves;
+  const int fresh_rows = rowroute::kFreshChunks * (1 + rowroute::kFreshMaxGpc) + kWaves + kPreQ;
   return static_cast<size_t>(fresh_rows * D + 2 * kWaves + kWaves * D +
                              kAttendMaxSplits * (D + 2)) * 4 + 64;
 }
