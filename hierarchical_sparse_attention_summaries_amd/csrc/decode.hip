@@ -48,11 +48,13 @@ struct StepArgs {
 };
 
 // Score words a scoring pass writes for each query row of a unit whose
-// sequence holds Tb > 0 keys: chunks [0, n_chunks), groups [0, n_groups).
+// sequence holds Tb > 0 keys: chunks [0, n_chunks), groups [0, n_groups). The
+// newest chunk cl is always kept (a row's own chunk, L <= cl) and the chunk
+// level ranks chunks 1..L-1 only, so its score is never needed or written.
 __device__ __forceinline__ void written_range(const RouteArgs& a, int Tb, int& n_chunks,
                                               int& n_groups) {
   const int cl = (Tb - 1) / a.C;
-  n_chunks = cl + 1;
+  n_chunks = cl;
   n_groups = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G);
 }
 
@@ -261,8 +263,16 @@ __device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s
   const bool pre_q = rpu <= kPreQ;
   uint4 qr0, qr1;
   q_issue<TQ, D>(a, row0, pre_q ? rpu : 0, qr0, qr1);
+  // Refreshed groups: with enough items, each has an item of its own (items
+  // 1..nfg), which sums the group's keys itself (the same bits as item 0's
+  // chunk summary) and scores it; item 0 then scores only the refreshed chunks
+  // below the newest, and its chunk summaries are needed only as outputs.
+  const int g0 = cf * a.gpc;
+  const int nfg = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G) - g0;
+  const bool own_items = s.items >= nfg + 2;
+  const int first_old = own_items ? nfg + 1 : 1;
+  constexpr int EPL = Elem<TQ>::kPer16;
   if (m == 0) {
-    constexpr int EPL = Elem<TQ>::kPer16;
     for (int c = cf; c <= cl; ++c) {
       chunk_summary<TQ, D, kWaves>(
           static_cast<const TQ*>(a.K), a.kv, b, a.Hkv, kv, a.T, Tb, a.C, a.G, c, s_part,
@@ -277,25 +287,46 @@ __device__ __forceinline__ void score_item(const RouteArgs& a, const StepArgs& s
           });
       __syncthreads();
     }
-    if (pre_q) {
-      q_stage<TQ, D>(a, rpu, qr0, qr1, s_q);
-      __syncthreads();
+    const int nfc = cl - cf;                  // scored chunks: cf .. cl - 1
+    const int n = nfc + (own_items ? 0 : nfg);
+    if (n > 0) {
+      if (pre_q) {
+        q_stage<TQ, D>(a, rpu, qr0, qr1, s_q);
+        __syncthreads();
+      }
+      // (one LDS base, so that these reads are known to be LDS reads and do
+      // not wait for outstanding global memory operations)
+      score_block<TQ, D>(
+          a, row0, rpu, n,
+          [&](int i) { return &s_fr[i < nfc ? i : rowroute::kFreshChunks + i - nfc][0]; },
+          [&](int i) { return i < nfc ? cf + i : a.n_c + g0 + i - nfc; }, s.scores, NS,
+          pre_q ? s_q : nullptr);
     }
-    const int nfc = cl - cf + 1;
-    const int g0 = cf * a.gpc;
-    const int nfg = min((cl + 1) * a.gpc, (Tb + a.G - 1) / a.G) - g0;
-    // (one LDS base, so that these reads are known to be LDS reads and do not
-    // wait for outstanding global memory operations)
+  } else if (m < first_old) {
+    // refreshed group g, summed by wave 0 (row 0 of s_fr as scratch)
+    const int g = g0 + m - 1;
+    if (threadIdx.x < kWave) {
+      float acc[EPL];
+      const int count = group_key_sum<TQ, D>(static_cast<const TQ*>(a.K), a.kv, b, a.Hkv, kv,
+                                             a.T, Tb, a.G, g, acc);
+      const float inv = 1.f / static_cast<float>(count);
+      constexpr int LPR = D / EPL;
+      if (lane_id() < LPR) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_fr[0][lane_id() * EPL + e] = acc[e] * inv;
+      }
+    }
+    if (pre_q) q_stage<TQ, D>(a, rpu, qr0, qr1, s_q);
+    __syncthreads();
     score_block<TQ, D>(
-        a, row0, rpu, nfc + nfg,
-        [&](int i) { return &s_fr[i < nfc ? i : rowroute::kFreshChunks + i - nfc][0]; },
-        [&](int i) { return i < nfc ? cf + i : a.n_c + g0 + i - nfc; }, s.scores, NS,
-        pre_q ? s_q : nullptr);
+        a, row0, rpu, 1, [&](int) { return &s_fr[0][0]; }, [&](int) { return a.n_c + g; },
+        s.scores, NS, pre_q ? s_q : nullptr);
   } else {
     // the older summaries: chunks [0, cf), then groups [0, cf * gpc)
     const int n_old = cf * (1 + a.gpc);
-    const int per = (n_old + s.items - 2) / (s.items - 1);
-    const int j0 = (m - 1) * per;
+    const int n_items = s.items - first_old;
+    const int per = (n_old + n_items - 1) / n_items;
+    const int j0 = (m - first_old) * per;
     const int j1 = min(n_old, j0 + per);
     if (j0 < j1) {
       score_block<TQ, D>(

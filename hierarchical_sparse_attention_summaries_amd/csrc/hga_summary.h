@@ -11,9 +11,52 @@
 
 namespace hga {
 
+// The sum of group g's keys (rows [g * G, min(g * G + G, Tb)) of (b, kv)), by
+// one wave: 16-byte loads, 8 in flight per lane, fp32 accumulation, then a
+// fold over the rows; lane l ends with dims [(l % LPR) * EPL, +EPL) of the sum
+// (every row added in a fixed order, so every caller gets the same bits).
+// Returns the group's row count.
+template <typename TK, int D>
+__device__ __forceinline__ int group_key_sum(const TK* __restrict__ K, const KvLayout& L, int b,
+                                             int Hkv, int kv, int T, int Tb, int G, int g,
+                                             float (&acc)[Elem<TK>::kPer16]) {
+  constexpr int EPL = Elem<TK>::kPer16;
+  constexpr int LPR = D / EPL;
+  constexpr int RPL = kWave / LPR;
+  constexpr int UNROLL = 8;
+  const int lane = lane_id();
+  const int col = (lane % LPR) * EPL;
+  const int sub = lane / LPR;
+  const int t0 = g * G;
+  const int t1 = min(t0 + G, Tb);
+  const int64_t off = kv_offset(L, b, Hkv, kv, T, D, t0);  // the group's rows are consecutive
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  if (off >= 0) {
+    const TK* Kg = K + off;
+    for (int base = 0; base < t1 - t0; base += RPL * UNROLL) {
+      uint4 raw[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int t = base + u * RPL + sub;
+        raw[u] = t < t1 - t0 ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float x[EPL];
+        widen(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<LPR>(acc[e]);
+  return t1 - t0;
+}
+
 // Wave w sums groups g_first + w, g_first + w + WAVES, ... of chunk c of
-// (b, kv): 16-byte loads, UNROLL in flight per lane, fp32 accumulation, then a
-// fold over the rows of the group. put_group(g, col, sums, count) runs on the
+// (b, kv) with group_key_sum. put_group(g, col, sums, count) runs on the
 // lanes holding columns col .. col+EPL-1 of group g (sums not yet divided);
 // the waves' group sums meet in s_part, and after a workgroup barrier
 // put_chunk(d, chunk_sum, count) runs on threads d < D.
@@ -24,8 +67,6 @@ __device__ __forceinline__ void chunk_summary(const TK* __restrict__ K, const Kv
                                               PutChunk put_chunk) {
   constexpr int EPL = Elem<TK>::kPer16;   // elements per lane per load
   constexpr int LPR = D / EPL;            // lanes per key row
-  constexpr int RPL = kWave / LPR;        // rows per wave-wide load
-  constexpr int UNROLL = 8;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int col = (lane % LPR) * EPL;
@@ -38,33 +79,9 @@ __device__ __forceinline__ void chunk_summary(const TK* __restrict__ K, const Kv
 #pragma unroll
   for (int e = 0; e < EPL; ++e) csum[e] = 0.f;
   for (int g = g_first + wave; g < g_end; g += WAVES) {
-    const int t0 = g * G;
-    const int t1 = min(t0 + G, Tb);
-    const int64_t off = kv_offset(L, b, Hkv, kv, T, D, t0);  // the group's rows are consecutive
     float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    if (off >= 0) {
-      const TK* Kg = K + off;
-      for (int base = 0; base < t1 - t0; base += RPL * UNROLL) {
-        uint4 raw[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int t = base + u * RPL + sub;
-          raw[u] = t < t1 - t0 ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          float x[EPL];
-          widen(raw[u], x);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] += x[e];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<LPR>(acc[e]);
-    if (sub == 0) put_group(g, col, acc, t1 - t0);
+    const int count = group_key_sum<TK, D>(K, L, b, Hkv, kv, T, Tb, G, g, acc);
+    if (sub == 0) put_group(g, col, acc, count);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) csum[e] += acc[e];
   }
