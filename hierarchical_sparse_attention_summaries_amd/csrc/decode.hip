@@ -370,10 +370,10 @@ __device__ __forceinline__ void write_refreshed(const RouteArgs& a, int u, const
 }
 
 // Dynamic LDS of the step: the row's scores [n_c + n_g] | kept chunks [cap] |
-// candidate group ids [cap * gpc] | chosen [max(k_c, k_g)] | the row's ids [k_g].
+// chosen [max(k_c, k_g)] | the row's ids [k_g].
 inline size_t step_lds_bytes(const RouteArgs& a) {
   const int cap = kept_capacity(a);
-  return static_cast<size_t>(a.n_c + a.n_g + cap + cap * a.gpc + max(a.k_c, a.k_g) + a.k_g) * 4;
+  return static_cast<size_t>(a.n_c + a.n_g + cap + max(a.k_c, a.k_g) + a.k_g) * 4;
 }
 
 template <typename T, int D, int E>
@@ -405,8 +405,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   float* s_cs = s_dyn;               // chunk scores [n_c]
   float* s_gs = s_cs + ra.n_c;       // group scores [n_g]
   int* s_kept = reinterpret_cast<int*>(s_gs + ra.n_g);
-  int* s_gid = s_kept + cap;
-  int* s_pick = s_gid + cap * ra.gpc;
+  int* s_pick = s_kept + cap;
   int* s_ids = s_pick + max(ra.k_c, ra.k_g);
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -502,24 +501,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   if (wave == 0) {
     int got = 0;
     if (!ok) n_kept = 0;  // a poisoned row routes to nothing
+    // Candidate t of level 2 is group s_kept[t / gpc] * gpc + t % gpc (kept
+    // chunks ascending, so the candidates ascend too).
+    const int gpc = ra.gpc;
+    const bool pow2 = (gpc & (gpc - 1)) == 0;
+    const int sh = __builtin_ctz(static_cast<unsigned>(gpc));
+    auto cand = [&](int t) {
+      const int k = pow2 ? t >> sh : t / gpc;
+      return s_kept[k] * gpc + (t - k * gpc);
+    };
     if (p >= 0 && ok) {
-      // level 2: the groups of the kept chunks that start at or before p;
-      // invalid candidates sit only at the end of the list (last kept chunk)
-      const int n_cand = n_kept * ra.gpc;
-      int n_valid = 0;
-      for (int t = lane; t < n_cand; t += kWave) {
-        const int g = s_kept[t / ra.gpc] * ra.gpc + t % ra.gpc;
-        s_gid[t] = g;
-        n_valid += (g < ra.n_g && static_cast<int64_t>(g) * ra.G <= p) ? 1 : 0;
-      }
-      n_valid = static_cast<int>(wave_add(static_cast<uint32_t>(n_valid)));
-      wave_lds_sync();
-      got = rowroute::wave_select<E>(n_valid, ra.k_g, [&](int t) { return s_gs[s_gid[t]]; },
+      // level 2: the groups of the kept chunks that start at or before p; the
+      // invalid ones are the last kept chunk's (chunk L's) groups after p
+      const int n_valid = (n_kept - 1) * gpc + min(gpc, p / ra.G - L * gpc + 1);
+      got = rowroute::wave_select<E>(n_valid, ra.k_g, [&](int t) { return s_gs[cand(t)]; },
                                      s_pick);
       wave_lds_sync();
     }
     for (int t = lane; t < ra.k_g; t += kWave) {
-      const int g = t < got ? s_gid[s_pick[t]] : -1;
+      const int g = t < got ? cand(s_pick[t]) : -1;
       s_ids[t] = g;
       if (split == 0) ra.group_idx[static_cast<size_t>(row) * ra.k_g + t] = g;
     }
@@ -641,7 +641,7 @@ bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int6
   // the score and partial words live in the workspace's zero-at-rest region
   if (step_words(rows, n_c + n_g, plan.n_splits, D).end > kZeroBytes) return false;
   const int64_t cap = std::min<int64_t>(k_c + 2, n_c);
-  const size_t lds = static_cast<size_t>(n_c + n_g + cap + cap * (C / G) + std::max(k_c, k_g) + k_g) * 4;
+  const size_t lds = static_cast<size_t>(n_c + n_g + cap + std::max(k_c, k_g) + k_g) * 4;
   return lds + step_static_lds(D) <= 160 * 1024;
 }
 
