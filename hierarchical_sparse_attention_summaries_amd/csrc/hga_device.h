@@ -197,12 +197,21 @@ __device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) 
   uint32_t thr = 0;
   for (int bit = 30; bit >= 0; bit -= 2) {
     const uint32_t t1 = thr | (1u << bit), t2 = thr | (2u << bit), t3 = thr | (3u << bit);
+    // all compares first, then the counts (a few percent faster than
+    // interleaving them)
+    uint64_t b1[E], b2[E], b3[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      b3[e] = ballot(key[e] >= t3);
+      b2[e] = ballot(key[e] >= t2);
+      b1[e] = ballot(key[e] >= t1);
+    }
     int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c1 += __popcll(ballot(key[e] >= t1));
-      c2 += __popcll(ballot(key[e] >= t2));
-      c3 += __popcll(ballot(key[e] >= t3));
+      c3 += __popcll(b3[e]);
+      c2 += __popcll(b2[e]);
+      c1 += __popcll(b1[e]);
     }
     int c = -1;
     if (c3 >= k) {
