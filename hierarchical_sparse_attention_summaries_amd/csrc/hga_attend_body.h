@@ -206,7 +206,10 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     m = m_new;
   };
 
-  if (a.G <= kAttendTile) {
+  // fp32 groups in 512-thread workgroups (256 VGPRs at most): one buffer, so
+  // that the tile does not spill
+  constexpr bool kDouble = !(sizeof(TKV) == 4 && kBodyThreads > kAttendThreads);
+  if (kDouble && a.G <= kAttendTile) {
     // One tile per group. Two register buffers: the next group's keys and
     // values are in flight while the current one is folded in.
     uint4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
@@ -223,7 +226,7 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
       if (b0 < b1) consume(b0, b1, kB, vB);
     }
   } else {
-    // Groups longer than a tile: walk their tiles one by one.
+    // Groups longer than a tile (or one buffer only): walk the tiles one by one.
     uint4 kA[NLD], vA[NLD];
     for (int e = e0; e < e1; ++e) {
       int t0, t1;

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kStageThreads) void gather_kernel(const T* K, const
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int64_t i = base + static_cast<int64_t>(u) * kStageThreads;
+      a[u] = c[u] = make_uint4(0, 0, 0, 0);
       if (i < n16) {
         a[u] = ks[i];
         c[u] = vs[i];
