@@ -463,7 +463,11 @@ def _same_attention(O_a, lse_a, O_b, lse_b, dtype):
     else:
         lim = torch.maximum(a.abs(), b.abs()) * 1e-5 + 1e-6
     assert bool((d <= lim).all()), f"O differs by up to {float(d.max()):.3g}"
-    assert float((lse_a - lse_b).abs().max()) <= 1e-4
+    # rows without keys have lse = -inf on both sides
+    assert torch.equal(torch.isneginf(lse_a), torch.isneginf(lse_b))
+    fin = torch.isfinite(lse_a)
+    if bool(fin.any()):
+        assert float((lse_a[fin] - lse_b[fin]).abs().max()) <= 1e-4
 
 
 def _zero_regions_are_zero():
@@ -518,6 +522,45 @@ def test_decode_step_equals_fresh_route_then_attend(case):
         from synth.inputs import Inputs
         inp2 = Inputs(w, inp.seed, inp.Q, Kc.float().cpu().numpy(), inp.V)
         check_workload(w, inp2, dict(cm=cm_d, gm=gm_d, cidx=c_d, gidx=g_d, O=O_d, lse=lse_d))
+
+
+def test_decode_step_one_launch_ragged_short_and_empty():
+    """One-launch decode step over a ragged dense batch holding an empty
+    sequence and one shorter than the number of new queries (its first query
+    sits before its first key): routes and summaries equal route_fresh_ex's bit
+    for bit, attention equals attend_ex's to fp32 rounding, rows without keys
+    give O = 0 and lse = -inf, and the workspace's zero region is left zero."""
+    w = DECODE_64K.with_(B=3, Hq=8, Hkv=2, T=4096, Nq=3, k_chunk=4, k_group=8, plants=1)
+    seq_lens = [w.T, 2, 0]
+    log(f"case decode-step-ragged-short-empty seq_lens={seq_lens}")
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    assert hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    layout = hga.Layout(seq_lens=lens)
+    cm, gm = hga.build_summaries_ex(K, w.chunk, w.group, layout=layout, seq_len=w.T)
+    for b, Tb in enumerate(seq_lens):   # the newest keys changed after the build
+        K[b, :, max(0, Tb - w.Nq):Tb] += 0.75
+    cm_d, gm_d = cm.clone(), gm.clone()
+    O_d, lse_d, c_d, g_d = hga.decode_step_ex(Q, K, V, cm_d, gm_d, w.T, w.chunk, w.group,
+                                              w.k_chunk, w.k_group, layout=layout)
+    cm_r, gm_r = cm.clone(), gm.clone()
+    c_r, g_r = hga.route_fresh_ex(Q, K, cm_r, gm_r, w.T, w.chunk, w.group, w.k_chunk,
+                                  w.k_group, layout=layout)
+    O_r, lse_r = hga.attend_ex(Q, K, V, g_r, w.group, layout=layout, seq_len=w.T)
+    torch.cuda.synchronize()
+    assert torch.equal(g_d, g_r) and torch.equal(c_d, c_r)
+    assert torch.equal(cm_d, cm_r) and torch.equal(gm_d, gm_r)
+    _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
+    # rows with no key at or before their position: the empty sequence, and
+    # the short sequence's first query (position 2 - 3 + 0 < 0)
+    for b, i in [(2, 0), (2, 1), (2, 2), (1, 0)]:
+        assert bool((g_d[b, :, i] == -1).all())
+        assert bool((O_d[b, :, i].float() == 0).all())
+        assert bool(torch.isneginf(lse_d[b, :, i]).all())
+    assert bool((g_d[1, :, 1:, 0] >= 0).all())   # the short sequence's later queries see keys
+    _zero_regions_are_zero()
 
 
 def test_decode_step_back_to_back_leaves_counters_zero():
