@@ -268,8 +268,10 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
                                                                  sacc[tb][rb], 0, 0, 0);
       }
     }
-    // Per row block: mask (routed group, causal), base-2 scale, online softmax.
-    // Token x of group g is taken iff the row routed g and x <= p - g * G.
+    // Per row block: mask (routed group, causal), online softmax. Token x of
+    // group g is taken iff the row routed g and x <= p - g * G. The running
+    // maximum m is kept in unscaled score units; p = 2^(s * sl2 - m * sl2) with
+    // one fused multiply-add.
     float p[kRB][2 * kSG][4];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tb = 2 * gi + h2;
-            sv[tb][i] = (h2 * 16 + a4 + i <= lim) ? sacc[tb][rb][i] * sl2 : -INFINITY;
+            sv[tb][i] = (h2 * 16 + a4 + i <= lim) ? sacc[tb][rb][i] : -INFINITY;
             mt = fmaxf(mt, sv[tb][i]);
           }
       }
@@ -293,18 +295,20 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
       const float m_new = fmaxf(m[rb], mt);
       // rescale only where a row's running maximum moved (rarely, once warm)
       if (ballot(m_new > m[rb]) != 0u) {
-        const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
+        const float corr =
+            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[rb] - m_new) * sl2);
         l[rb] *= corr;
 #pragma unroll
         for (int d = 0; d < kTD / 16; ++d) o[rb][d] *= corr;
       }
       m[rb] = m_new;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // rows with nothing yet: p = 0
+      // rows with nothing yet: p = 0
+      const float nm = m_new == -INFINITY ? 0.f : -m_new * sl2;
 #pragma unroll
       for (int tb = 0; tb < 2 * kSG; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[rb][tb][i] = __builtin_amdgcn_exp2f(sv[tb][i] - m_use);
+          p[rb][tb][i] = __builtin_amdgcn_exp2f(fmaf(sv[tb][i], sl2, nm));
           l[rb] += p[rb][tb][i];
         }
     }
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
         *reinterpret_cast<uint2*>(O + orow + d * 16 + a4) = make_uint2(w[0], w[1]);
       }
       if (a.lse && lane < 16)
-        a.lse[row0 + my_r] = lt > 0.f ? (m[rb] + log2f(lt)) * kLn2 : -INFINITY;
+        a.lse[row0 + my_r] = lt > 0.f ? (m[rb] * sl2 + log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
