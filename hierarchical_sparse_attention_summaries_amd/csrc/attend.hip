@@ -16,8 +16,7 @@ constexpr int kMaxSplits = kAttendMaxSplits;
 template <typename TKV, int D>
 __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a, int groups_per_wave,
                                                                 int n_splits, int row_base) {
-  attend_body<TKV, D, false>(a, groups_per_wave, n_splits, row_base, static_cast<int>(blockIdx.x),
-                             nullptr);
+  attend_body<TKV, D>(a, groups_per_wave, n_splits, row_base, static_cast<int>(blockIdx.x));
 }
 
 template <typename TKV, int D>

@@ -539,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     for (int t = static_cast<int>(threadIdx.x); t < n_chunks + n_groups; t += kThreads)
       store_shared_i32(words + (t < n_chunks ? t : ra.n_c + t - n_chunks), 0);
   };
-  attend_body<T, D, false, kWaves, true, decltype(zero_row), true>(
-      aa, st.groups_per_wave, st.n_splits, 0, bid, nullptr, s_ids, !ok, zero_row);
+  attend_body<T, D, kWaves, true, decltype(zero_row), true>(aa, st.groups_per_wave, st.n_splits,
+                                                           0, bid, s_ids, !ok, zero_row);
   if (bid < U) write_refreshed<D>(ra, bid, s_fr);
 }
 

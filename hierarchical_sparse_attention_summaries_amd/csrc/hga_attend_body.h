@@ -24,34 +24,12 @@ constexpr int kAttendWaves = kAttendThreads / kWave;
 constexpr int kAttendTile = 32;        // tokens per gather tile
 constexpr int kAttendMaxSplits = 32;   // workgroups per row at most (the plan guarantees it)
 
-// Bounded wait, by the whole workgroup, for *flag != 0 (set with agent-scope
-// stores after the data it guards). Returns false if it gave up.
-__device__ __forceinline__ bool wait_ready(const unsigned* flag, bool* s_ok) {
-  if (threadIdx.x == 0) {
-    bool ok = false;
-    for (int it = 0; it < (1 << 20); ++it) {
-      if (__hip_atomic_load(const_cast<unsigned*>(flag), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-        ok = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(4);
-    }
-    *s_ok = ok;
-  }
-  __syncthreads();
-  return *s_ok;
-}
-
 struct NoRowHook {
   __device__ void operator()() const {}
 };
 
 // One attention workgroup: row `row_base + bid / n_splits`, split
-// `bid % n_splits`. With `ready` set (routing and attention in one launch), it
-// first waits until the row's routing workgroup has published the row's group
-// ids (bounded wait), reads them coherently, and the row's last workgroup
-// clears the flag again. With LDS_IDS the row's group ids are already in LDS
+// `bid % n_splits`. With LDS_IDS the row's group ids are already in LDS
 // (s_ids, k_group entries), chosen by this workgroup itself; `poisoned` then
 // marks a row whose routing could not be completed (its outputs become NaN).
 // `row_done` is called by every thread of the workgroup that finishes the row,
@@ -62,12 +40,11 @@ struct NoRowHook {
 // theirs and are done, and split 0 polls them (bounded; NaN outputs if one
 // does not arrive in time), merges, and zeroes them again; no counters.
 // Returns true in the workgroup that wrote the row's outputs.
-template <typename TKV, int D, bool WAIT, int WAVES = kAttendWaves, bool LDS_IDS = false,
+template <typename TKV, int D, int WAVES = kAttendWaves, bool LDS_IDS = false,
           typename RowHook = NoRowHook, bool POLL_MERGE = false>
 __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_wave, int n_splits,
-                                            int row_base, int bid, unsigned* ready,
-                                            const int* s_ids = nullptr, bool poisoned = false,
-                                            RowHook row_done = RowHook{}) {
+                                            int row_base, int bid, const int* s_ids = nullptr,
+                                            bool poisoned = false, RowHook row_done = RowHook{}) {
   constexpr int kBodyThreads = WAVES * kWave;
   constexpr int EPL = Elem<TKV>::kPer16;
   constexpr int LPR = D / EPL;        // lanes per token row
@@ -79,7 +56,6 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
   __shared__ float s_m[WAVES], s_l[WAVES];
   __shared__ float s_o[WAVES][D];
   __shared__ bool s_last;
-  __shared__ bool s_flag;
   __shared__ float s_part[kAttendMaxSplits * (D + 2)];
 
   const int row = row_base + bid / n_splits;
@@ -114,7 +90,6 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
 
   const int32_t* gl = a.group_idx + static_cast<size_t>(row) * a.k_g;
   bool timed_out = poisoned;
-  if constexpr (WAIT) timed_out = !wait_ready(ready + row, &s_flag);
   const int e0 = (split * WAVES + wave) * groups_per_wave;
   const int e1 = min(e0 + groups_per_wave, a.k_g);
   const int n_g = (a.T + a.G - 1) / a.G;
@@ -130,8 +105,6 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
       if (j < e1) {
         if constexpr (LDS_IDS) {
           g_lane = s_ids[j];
-        } else if constexpr (WAIT) {
-          g_lane = load_shared_i32(gl + j);
         } else {
           g_lane = gl[j];
         }
@@ -270,12 +243,6 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
   if (timed_out) Lsum = __builtin_nanf("");
 
   auto finish = [&](float Mx, float Lx, float ox) {
-    // the row is done: clear its flag for the next call (never on a timeout,
-    // whose outputs are NaN)
-    if constexpr (WAIT) {
-      if (d == 0 && !timed_out) __hip_atomic_store(ready + row, 0u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-    }
     if (timed_out) {
       Lx = 1.f;
       ox = __builtin_nanf("");

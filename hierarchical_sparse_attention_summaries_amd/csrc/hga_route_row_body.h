@@ -6,8 +6,7 @@
 // the k_group best of them. Everything between the two summary reads stays in
 // LDS, so a row costs two memory round trips and no workgroup waits for or
 // hands data to another. Optionally it first refreshes the summaries of the
-// sequence's newest chunks from K, and/or publishes its group ids to attention
-// workgroups of the same launch.
+// sequence's newest chunks from K.
 #pragma once
 
 #include <algorithm>
@@ -131,29 +130,6 @@ __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out
 constexpr int kFreshChunks = 2;   // chunks a refresh of <= C newest keys can touch
 constexpr int kFreshMaxGpc = 16;  // groups per chunk the refresh keeps in LDS
 
-// Index stores of the routing result: plain, or (when attention workgroups of
-// the same launch read them) agent-coherent.
-template <bool PUBLISH>
-__device__ __forceinline__ void put_idx(int32_t* p, int32_t v) {
-  if constexpr (PUBLISH) {
-    store_shared_i32(p, v);
-  } else {
-    *p = v;
-  }
-}
-
-// Marks a row's group ids as ready for the attention workgroups of the same
-// launch: every thread's index stores are performed first.
-template <bool PUBLISH>
-__device__ __forceinline__ void publish_row(unsigned* ready, int row) {
-  if constexpr (PUBLISH) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(ready + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // Dynamic LDS bytes of route_row_body: chunk scores, candidate scores and
 // group ids, kept chunks, and the chosen ids of either level.
 inline size_t route_row_lds_bytes(int64_t n_c, int64_t cap, int64_t gpc, int k_c, int k_g) {
@@ -172,9 +148,8 @@ inline size_t route_row_static_lds(int64_t D, bool fresh) {
 // without opting in to more.
 constexpr size_t kRowRouteMaxLds = 65536;
 
-template <typename TQ, int D, int E, bool FRESH, bool PUBLISH, bool BIG>
-__device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, float* s_dyn,
-                                               unsigned* ready) {
+template <typename TQ, int D, int E, bool FRESH, bool BIG>
+__device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, float* s_dyn) {
   // LDS: chunk scores [n_c] | candidate scores [cap * gpc] | candidate group ids
   // [cap * gpc] | kept chunks [cap] | chosen [max]
   const int cap = kept_capacity(a);
@@ -207,8 +182,7 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
       for (int t = threadIdx.x; t < a.k_c + 2; t += kThreads)
         a.chunk_idx[static_cast<size_t>(row) * (a.k_c + 2) + t] = -1;
     for (int t = threadIdx.x; t < a.k_g; t += kThreads)
-      put_idx<PUBLISH>(a.group_idx + static_cast<size_t>(row) * a.k_g + t, -1);
-    publish_row<PUBLISH>(ready, row);
+      a.group_idx[static_cast<size_t>(row) * a.k_g + t] = -1;
     return;
   }
   const int L = p / a.C;
@@ -352,10 +326,8 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     int32_t* out = a.group_idx + static_cast<size_t>(row) * a.k_g;
-    for (int t = lane; t < a.k_g; t += kWave)
-      put_idx<PUBLISH>(out + t, t < got ? s_gid[s_pick[t]] : -1);
+    for (int t = lane; t < a.k_g; t += kWave) out[t] = t < got ? s_gid[s_pick[t]] : -1;
   }
-  publish_row<PUBLISH>(ready, row);
 }
 
 

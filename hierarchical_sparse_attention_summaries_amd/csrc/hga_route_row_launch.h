@@ -11,7 +11,7 @@ namespace rowroute {
 template <typename TQ, int D, int E, bool FRESH, bool BIG>
 __global__ __launch_bounds__(kThreads) void route_row_kernel(RouteArgs a) {
   extern __shared__ float s_dyn[];
-  route_row_body<TQ, D, E, FRESH, false, BIG>(a, static_cast<int>(blockIdx.x), s_dyn, nullptr);
+  route_row_body<TQ, D, E, FRESH, BIG>(a, static_cast<int>(blockIdx.x), s_dyn);
 }
 
 // Workgroups of the row route: rows of one (sequence, KV head) share an XCD,
