@@ -36,7 +36,9 @@
  *     before the workspace's first use (e.g. allocate it zeroed). Every call
  *     leaves them at zero, so one workspace (large enough for each call) can
  *     serve calls of any shape in turn. Calls that may run concurrently must
- *     not share a workspace.
+ *     not share a workspace. After a call that returned HGA_ERR_HIP, or whose
+ *     kernels faulted, the region's contents are unspecified: zero it again
+ *     before the workspace's next use.
  */
 #ifndef HGA_H
 #define HGA_H
