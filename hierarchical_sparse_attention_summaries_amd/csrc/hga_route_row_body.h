@@ -95,6 +95,7 @@ __device__ __forceinline__ void score_rows(const float (&q)[8], int from, int n,
 // groups at a 64K context) takes one pass. Larger grids keep to 128 VGPRs so
 // that two workgroups share a CU.
 constexpr int kChunkPass = 8;
+constexpr int kChunkPassLeanFresh = 4;  // leaves registers for the refresh's loads
 constexpr int kGroupPassBig = 16;
 constexpr int kGroupPassLean = 8;
 
@@ -213,7 +214,8 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
 
   // Level 1's first pass of chunk-summary loads (in the big form it goes out
   // now, before the refresh below; it skips the chunks the refresh rewrites).
-  using P1 = RowPass<D, kChunkPass>;
+  constexpr int kL1 = (FRESH && !BIG) ? kChunkPassLeanFresh : kChunkPass;
+  using P1 = RowPass<D, kL1>;
   P1 pass1;
   pass1.clear();
   const int base1 = P1::base();
@@ -228,14 +230,62 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
   __shared__ float s_fc[FRESH ? kFreshChunks : 1][D];
   __shared__ float s_fg[FRESH ? kFreshChunks * kFreshMaxGpc : 1][D];
   __shared__ float s_part[FRESH ? kWaves : 1][D];
+  using KR = KeyRowLoads<TQ, D>;
+  constexpr int EPL = KR::EPL;
+  const int Tb = route_seq_len(a, b);
+  float* cm_w = const_cast<float*>(cm);
+  float* gm_w = const_cast<float*>(gm);
+  // Early refresh: when all the new keys lie in one chunk (always so in
+  // decode), that chunk is every row's own chunk L, which is kept whatever its
+  // score, so level 1 needs nothing from the refresh. Each wave then issues the
+  // loads of one of its groups first (the lean form, which keeps to 128 VGPRs,
+  // scores level 1 in smaller passes to leave room for them), they stay in
+  // flight while level 1 scores the older chunks, and the waves fold them
+  // while wave 0 ranks the chunks (wave 0 folds its own after). Same rows,
+  // lanes and order as chunk_summary, so the same bits.
+  bool early = false;
+  int g_first = 0, n_fg = 0, fg_rows = 0;
+  KR fresh_rows;
+  auto issue_fresh = [&]() {
+    fresh_rows.clear();
+    if (wave < n_fg) {
+      const int64_t off =
+          group_rows(a.kv, b, a.Hkv, kv, a.T, D, Tb, a.G, g_first + wave, &fg_rows);
+      if (off >= 0) fresh_rows.issue(static_cast<const TQ*>(a.K) + off, 0, fg_rows);
+    }
+  };
   if constexpr (FRESH) {
-    constexpr int EPL = Elem<TQ>::kPer16;
-    const int Tb = route_seq_len(a, b);
     cf = max(0, Tb - a.Nq) / a.C;
     cl = (Tb - 1) / a.C;
-    float* cm_w = const_cast<float*>(cm);
-    float* gm_w = const_cast<float*>(gm);
-    for (int c = cf; c <= cl; ++c) {
+    g_first = cf * a.gpc;
+    n_fg = min(g_first + a.gpc, (Tb + a.G - 1) / a.G) - g_first;
+    early = cf == cl && n_fg <= kWaves && a.G <= KR::kRows;
+    if (early) issue_fresh();
+  }
+  // folds this wave's early-refresh group: mean to LDS, sum to s_part (the
+  // means go to memory at the end: on gfx950 a wait for loads also waits for
+  // every store issued before them, so stores here would hold up level 2)
+  auto fold_fresh = [&]() {
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    fresh_rows.add_to(acc);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<KR::LPR>(acc[e]);
+    const int col = (lane % KR::LPR) * EPL;
+    if (lane / KR::LPR == 0) {
+      if (wave < n_fg) {
+        const int g = g_first + wave;
+        const float inv = 1.f / static_cast<float>(fg_rows);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_fg[g - cf * a.gpc][col + e] = acc[e] * inv;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_part[wave][col + e] = 0.f + (wave < n_fg ? acc[e] : 0.f);
+    }
+  };
+  if constexpr (FRESH) {
+    for (int c = cf; c <= cl && !early; ++c) {
       chunk_summary<TQ, D, kWaves>(
           static_cast<const TQ*>(a.K), a.kv, b, a.Hkv, kv, a.T, Tb, a.C, a.G, c, s_part,
           [&](int g, int col, const float (&sum)[EPL], int count) {
@@ -258,12 +308,15 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
   // chunks below c_fresh from memory, the refreshed ones (c_fresh..L) from LDS
   auto lds_chunk = [&](int c) { return &s_fc[FRESH ? c - cf : 0][0]; };
 
-  // Level 1: chunks 0..L.
-  if constexpr (!BIG) pass1.load(base1, 0, min(L + 1, c_fresh), mem_chunk);
-  pass1.load(base1, c_fresh, L + 1, lds_chunk);
-  pass1.dot(q, base1, L + 1, s_cs);
-  score_rows<D, kChunkPass>(q, P1::kRows, L + 1, c_fresh, mem_chunk, lds_chunk, s_cs);
+  // Level 1: chunks 0..L (0..L-1 after an early refresh: chunk L's score is
+  // never used, and its summary is not ready yet).
+  const int n_l1 = early ? L : L + 1;
+  if constexpr (!BIG) pass1.load(base1, 0, min(n_l1, c_fresh), mem_chunk);
+  pass1.load(base1, c_fresh, n_l1, lds_chunk);
+  pass1.dot(q, base1, n_l1, s_cs);
+  score_rows<D, kL1>(q, P1::kRows, n_l1, c_fresh, mem_chunk, lds_chunk, s_cs);
   __syncthreads();
+  if (FRESH && early && wave != 0) fold_fresh();
   if (wave == 0) {
     int n_kept;
     if (L + 1 <= a.k_c + 2) {
@@ -290,8 +343,15 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
       s_n_kept = n_kept;
       s_n_old = n_old;
     }
+    if (FRESH && early) fold_fresh();
   }
   __syncthreads();
+  if (FRESH && early && static_cast<int>(threadIdx.x) < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += s_part[w][threadIdx.x];
+    s_fc[0][threadIdx.x] = sum / static_cast<float>(min(a.C, Tb - cf * a.C));
+  }
   const int n_kept = s_n_kept;
   // candidate t (in kept-chunk order) is group s_gid[t]
   for (int t = threadIdx.x; t < n_kept * a.gpc; t += kThreads)
@@ -316,6 +376,12 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
       },
       [&](int t) { return &s_fg[FRESH ? s_gid[t] - cf * a.gpc : 0][0]; }, s_gs);
   __syncthreads();
+  if (FRESH && early && wave != 0) {  // the refreshed means, while wave 0 selects
+    const int t0 = static_cast<int>(threadIdx.x) - kWave;
+    for (int t = t0; t < n_fg * D; t += kThreads - kWave)
+      gm_w[static_cast<size_t>(g_first) * D + t] = s_fg[t / D][t % D];
+    for (int t = t0; t < D; t += kThreads - kWave) cm_w[static_cast<size_t>(cf) * D + t] = s_fc[0][t];
+  }
   if (wave == 0) {
     // Invalid candidates sit only in the last kept chunk (after p or past the
     // end), i.e. at the end of the list: select among the valid prefix.

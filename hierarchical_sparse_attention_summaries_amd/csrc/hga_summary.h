@@ -11,48 +11,79 @@
 
 namespace hga {
 
+// One wave's loads of up to kRows consecutive key rows (16 bytes per lane,
+// 8 in flight): lane l takes dims [(l % LPR) * EPL, +EPL) of rows
+// u * RPL + l / LPR. Issuing and adding are separate so that a caller can
+// keep the loads in flight across other work.
+template <typename TK, int D>
+struct KeyRowLoads {
+  static constexpr int EPL = Elem<TK>::kPer16;  // elements per lane per load
+  static constexpr int LPR = D / EPL;           // lanes per key row
+  static constexpr int RPL = kWave / LPR;       // rows per load instruction
+  static constexpr int UNROLL = 8;
+  static constexpr int kRows = RPL * UNROLL;
+  uint4 raw[UNROLL];
+
+  // rows [base, base + kRows) of the n rows at Kg (rows past n read as zero)
+  __device__ __forceinline__ void issue(const TK* __restrict__ Kg, int base, int n) {
+    const int lane = lane_id();
+    const int col = (lane % LPR) * EPL;
+    const int sub = lane / LPR;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int t = base + u * RPL + sub;
+      raw[u] = t < n ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) raw[u] = make_uint4(0, 0, 0, 0);
+  }
+  // acc += the rows, in row-slot order
+  __device__ __forceinline__ void add_to(float (&acc)[EPL]) const {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      float x[EPL];
+      widen(raw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+    }
+  }
+};
+
+// Where group g of (b, kv) starts in K (its rows are consecutive) and how many
+// of its rows lie below Tb; the offset is negative where no page holds it.
+__device__ __forceinline__ int64_t group_rows(const KvLayout& L, int b, int Hkv, int kv, int T,
+                                              int D, int Tb, int G, int g, int* n) {
+  const int t0 = g * G;
+  *n = min(t0 + G, Tb) - t0;
+  return kv_offset(L, b, Hkv, kv, T, D, t0);
+}
+
 // The sum of group g's keys (rows [g * G, min(g * G + G, Tb)) of (b, kv)), by
-// one wave: 16-byte loads, 8 in flight per lane, fp32 accumulation, then a
-// fold over the rows; lane l ends with dims [(l % LPR) * EPL, +EPL) of the sum
-// (every row added in a fixed order, so every caller gets the same bits).
-// Returns the group's row count.
+// one wave: KeyRowLoads passes with fp32 accumulation, then a fold over the
+// rows; lane l ends with dims [(l % LPR) * EPL, +EPL) of the sum (every row
+// added in a fixed order, so every caller gets the same bits). Returns the
+// group's row count.
 template <typename TK, int D>
 __device__ __forceinline__ int group_key_sum(const TK* __restrict__ K, const KvLayout& L, int b,
                                              int Hkv, int kv, int T, int Tb, int G, int g,
                                              float (&acc)[Elem<TK>::kPer16]) {
-  constexpr int EPL = Elem<TK>::kPer16;
-  constexpr int LPR = D / EPL;
-  constexpr int RPL = kWave / LPR;
-  constexpr int UNROLL = 8;
-  const int lane = lane_id();
-  const int col = (lane % LPR) * EPL;
-  const int sub = lane / LPR;
-  const int t0 = g * G;
-  const int t1 = min(t0 + G, Tb);
-  const int64_t off = kv_offset(L, b, Hkv, kv, T, D, t0);  // the group's rows are consecutive
+  using R = KeyRowLoads<TK, D>;
+  int n;
+  const int64_t off = group_rows(L, b, Hkv, kv, T, D, Tb, G, g, &n);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < R::EPL; ++e) acc[e] = 0.f;
   if (off >= 0) {
-    const TK* Kg = K + off;
-    for (int base = 0; base < t1 - t0; base += RPL * UNROLL) {
-      uint4 raw[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int t = base + u * RPL + sub;
-        raw[u] = t < t1 - t0 ? ld16(Kg + static_cast<size_t>(t) * D + col) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        float x[EPL];
-        widen(raw[u], x);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
-      }
+    for (int base = 0; base < n; base += R::kRows) {
+      R r;
+      r.issue(K + off, base, n);
+      r.add_to(acc);
     }
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = across_rows_sum<LPR>(acc[e]);
-  return t1 - t0;
+  for (int e = 0; e < R::EPL; ++e) acc[e] = across_rows_sum<R::LPR>(acc[e]);
+  return n;
 }
 
 // Wave w sums groups g_first + w, g_first + w + WAVES, ... of chunk c of
