@@ -386,33 +386,52 @@ def test_one_workspace_serves_calls_of_different_shapes():
         check_workload(w, inp, dict(cm=cm, gm=gm, cidx=cidx, gidx=gidx, O=O, lse=lse))
 
 
-@pytest.mark.parametrize("case", ["dense", "paged", "fallback-many-rows"])
+@pytest.mark.parametrize("case", ["dense", "paged", "fallback-many-rows", "paged-crossing",
+                                  "lean-crossing", "gpc16"])
 def test_route_fresh_equals_update_then_route(case):
     """hga_route_fresh_ex (refresh of the newest keys' chunks fused into
     routing) gives the summaries and routes of update-then-route, bit for bit,
-    and those match the oracle on the new keys."""
+    and those match the oracle on the new keys. The crossing cases put the
+    newest keys of some sequences on both sides of a chunk boundary, in the
+    one-workgroup-per-CU form and in the two-per-CU form (512 rows); gpc16 has
+    16 groups per chunk, more than a workgroup has waves."""
     log(f"case route-fresh-{case}")
+    seq_lens, paged = None, case in ("paged", "paged-crossing")
     if case == "fallback-many-rows":
         w = DECODE_64K.with_(B=40, T=4096, k_chunk=2, k_group=4, plants=1)
+    elif case == "lean-crossing":
+        w = DECODE_64K.with_(B=8, T=4096, Nq=2, k_chunk=2, k_group=4, plants=1)
+        seq_lens = [w.T if b % 2 == 0 else 15 * w.chunk + 1 for b in range(w.B)]
+    elif case == "gpc16":
+        w = DECODE_64K.with_(B=2, T=8192, group=16, k_chunk=4, k_group=16, plants=2)
     else:
         w = DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2)
+        if case == "paged":
+            seq_lens = [w.T, w.T - 100]
+        elif case == "paged-crossing":
+            seq_lens = [w.T, 31 * w.chunk + 1]
     inp = generate(w)
     Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
     layout, Kc, Vc = None, K, V
-    if case == "paged":
-        seq_lens = [w.T, w.T - 100]
-        kp, vp, table, n_pages = _pages(w, inp, seq_lens, 64)
+    if seq_lens is not None:
         lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
-        layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
-        Kc, Vc = kp, vp
+        if paged:
+            kp, vp, table, n_pages = _pages(w, inp, seq_lens, 64)
+            layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
+            Kc, Vc = kp, vp
+        else:
+            layout = hga.Layout(seq_lens=lens)
     cm, gm = hga.build_summaries_ex(Kc, w.chunk, w.group, layout=layout, seq_len=w.T)
     # the newest keys change after the summaries were built (a decode step appended them)
-    if case == "paged":
-        for b, Tb in enumerate(seq_lens):
-            for t in (Tb - 2, Tb - 1):
-                Kc[int(table[b, t // 64]), :, t % 64] += 0.75
-    else:
+    if seq_lens is None:
         Kc[:, :, -w.Nq:] += 0.75
+    else:
+        for b, Tb in enumerate(seq_lens):
+            for t in range(Tb - w.Nq, Tb):
+                if paged:
+                    Kc[int(table[b, t // 64]), :, t % 64] += 0.75
+                else:
+                    Kc[b, :, t] += 0.75
     cm_f, gm_f = cm.clone(), gm.clone()
     _, g_fresh = hga.route_fresh_ex(Q, Kc, cm_f, gm_f, w.T, w.chunk, w.group, w.k_chunk,
                                     w.k_group, layout=layout)
@@ -423,15 +442,17 @@ def test_route_fresh_equals_update_then_route(case):
     cm_b, gm_b = hga.build_summaries_ex(Kc, w.chunk, w.group, layout=layout, seq_len=w.T)
     torch.cuda.synchronize()
     assert torch.equal(g_fresh, g_ref)
-    if case != "paged":
+    if seq_lens is None:
         assert torch.equal(cm_f, cm_r) and torch.equal(gm_f, gm_r)
         assert torch.equal(cm_f, cm_b) and torch.equal(gm_f, gm_b)
     else:
         for b, Tb in enumerate(seq_lens):
             nc, ng = -(-Tb // w.chunk), -(-Tb // w.group)
+            assert torch.equal(cm_f[b, :, :nc], cm_r[b, :, :nc])
+            assert torch.equal(gm_f[b, :, :ng], gm_r[b, :, :ng])
             assert torch.equal(cm_f[b, :, :nc], cm_b[b, :, :nc])
             assert torch.equal(gm_f[b, :, :ng], gm_b[b, :, :ng])
-    if case == "dense":   # and the oracle on the modified keys agrees
+    if case in ("dense", "gpc16"):   # and the oracle on the modified keys agrees
         from synth.inputs import Inputs
         inp2 = Inputs(w, inp.seed, inp.Q, Kc.float().cpu().numpy(), inp.V)
         cidx, gidx = hga.route(Q, cm_b, gm_b, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
