@@ -97,7 +97,7 @@ __device__ __forceinline__ void score_rows(const float (&q)[8], int from, int n,
 constexpr int kChunkPass = 8;
 constexpr int kChunkPassLeanFresh = 4;  // leaves registers for the refresh's loads
 constexpr int kGroupPassBig = 16;
-constexpr int kGroupPassLean = 8;
+constexpr int kGroupPassLean = 9;
 
 // Top-k of n keys held in LDS (`score(i)` gives item i's float score), by one
 // wave; writes the chosen item ids ascending to out[0..k) and returns how many.
