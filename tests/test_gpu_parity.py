@@ -387,14 +387,15 @@ def test_one_workspace_serves_calls_of_different_shapes():
 
 
 @pytest.mark.parametrize("case", ["dense", "paged", "fallback-many-rows", "paged-crossing",
-                                  "lean-crossing", "gpc16"])
+                                  "lean-crossing", "gpc16", "f32-d64"])
 def test_route_fresh_equals_update_then_route(case):
     """hga_route_fresh_ex (refresh of the newest keys' chunks fused into
     routing) gives the summaries and routes of update-then-route, bit for bit,
     and those match the oracle on the new keys. The crossing cases put the
     newest keys of some sequences on both sides of a chunk boundary, in the
     one-workgroup-per-CU form and in the two-per-CU form (512 rows); gpc16 has
-    16 groups per chunk, more than a workgroup has waves."""
+    16 groups per chunk, more than a workgroup has waves; f32-d64 refreshes
+    fp32 keys of 64 dims (one load pass per group, as bf16 keys)."""
     log(f"case route-fresh-{case}")
     seq_lens, paged = None, case in ("paged", "paged-crossing")
     if case == "fallback-many-rows":
@@ -404,6 +405,8 @@ def test_route_fresh_equals_update_then_route(case):
         seq_lens = [w.T if b % 2 == 0 else 15 * w.chunk + 1 for b in range(w.B)]
     elif case == "gpc16":
         w = DECODE_64K.with_(B=2, T=8192, group=16, k_chunk=4, k_group=16, plants=2)
+    elif case == "f32-d64":
+        w = DECODE_64K.with_(B=2, T=4096, D=64, k_chunk=3, k_group=12, plants=1, dtype="f32")
     else:
         w = DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2)
         if case == "paged":
@@ -452,7 +455,7 @@ def test_route_fresh_equals_update_then_route(case):
             assert torch.equal(gm_f[b, :, :ng], gm_r[b, :, :ng])
             assert torch.equal(cm_f[b, :, :nc], cm_b[b, :, :nc])
             assert torch.equal(gm_f[b, :, :ng], gm_b[b, :, :ng])
-    if case in ("dense", "gpc16"):   # and the oracle on the modified keys agrees
+    if case in ("dense", "gpc16", "f32-d64"):   # and the oracle on the modified keys agrees
         from synth.inputs import Inputs
         inp2 = Inputs(w, inp.seed, inp.Q, Kc.float().cpu().numpy(), inp.V)
         cidx, gidx = hga.route(Q, cm_b, gm_b, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
