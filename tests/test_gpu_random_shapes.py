@@ -22,7 +22,7 @@ from tests.gpu_runner import check_workload, log, run_hip, to_dev
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 28
+N_CASES = 48
 N_MANY_ROWS = 4   # the last cases: > 1024 query rows, not the MFMA route
 N_TILES = 6       # then: the tile attention
 
@@ -94,3 +94,11 @@ def test_random_shape(seed):
         lim = torch.maximum(a.abs(), b.abs()) * (2.0 ** -7 if w.dtype == "bf16" else 1e-5) + 1e-6
         assert bool(((a - b).abs() <= lim).all())
         assert float((lse - out["lse"]).abs().max()) <= 1e-4
+        # the fused refresh-and-route on summaries that are already current
+        # rewrites them with the same bits and routes as the separate calls
+        cm_f, gm_f = cm.clone(), gm.clone()
+        c_f, g_f = hga.route_fresh_ex(Q, K, cm_f, gm_f, w.T, w.chunk, w.group, w.k_chunk,
+                                      w.k_group)
+        torch.cuda.synchronize()
+        assert torch.equal(cm_f, out["cm"]) and torch.equal(gm_f, out["gm"])
+        assert torch.equal(g_f, out["gidx"]) and torch.equal(c_f, out["cidx"])
