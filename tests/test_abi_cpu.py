@@ -209,3 +209,22 @@ def test_attend_staged_rejects_before_launch():
     assert f(ctypes.byref(s), *bad) == LAYOUT
     bad = list(args); bad[5] = 0
     assert f(ctypes.byref(s), *bad) == PARAM
+
+
+def test_package_without_library_fails_loudly(tmp_path):
+    """There is no CPU fallback: a copy of the package without libhga.so
+    refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(hga.__file__)
+    dst = tmp_path / os.path.basename(src)
+    dst.mkdir()
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), dst / name)
+    r = subprocess.run([sys.executable, "-c", f"import {os.path.basename(src)}"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libhga.so not built" in r.stderr
