@@ -174,6 +174,17 @@ def test_sweep_b16(T):
     out = run_hip(w, inp)
     b_list = None if T <= 16384 else [0, 7, 15]
     check_workload(w, inp, out, b_list=b_list)
+    # the decode step the benchmark times at batch 16 (refreshing route, then
+    # attention) against the separate calls checked above: summaries and routes
+    # bit for bit, attention to fp32 rounding
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    cm, gm = hga.build_summaries(K, w.chunk, w.group)
+    O, lse, c_d, g_d = hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk,
+                                          w.k_group)
+    torch.cuda.synchronize()
+    assert torch.equal(cm, out["cm"]) and torch.equal(gm, out["gm"])
+    assert torch.equal(g_d, out["gidx"]) and torch.equal(c_d, out["cidx"])
+    _same_attention(O, lse, out["O"], out["lse"], w.dtype)
 
 
 def test_update_summaries_bit_identical_to_build():
