@@ -728,3 +728,11 @@ def test_attend_staged_host_tier_b4_t262144():
     distinct = sum(len(np.unique(g[b, kv * r:(kv + 1) * r][g[b, kv * r:(kv + 1) * r] >= 0]))
                    for b in range(w.B) for kv in range(w.Hkv))
     assert distinct < 0.75 * int((g >= 0).sum())
+    # the benchmark's host-tier step routes with the refresh reading K from
+    # host memory: same summaries and routes, bit for bit
+    cm_f, gm_f = out["cm"].clone(), out["gm"].clone()
+    c_f, g_f = hga.route_fresh_ex(out["Q"], out["K"], cm_f, gm_f, w.T, w.chunk, w.group,
+                                  w.k_chunk, w.k_group)
+    torch.cuda.synchronize()
+    assert torch.equal(cm_f, out["cm"]) and torch.equal(gm_f, out["gm"])
+    assert torch.equal(g_f, out["gidx"]) and torch.equal(c_f, out["cidx"])
