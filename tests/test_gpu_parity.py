@@ -130,6 +130,15 @@ def test_prefill_4096_on_61440_sampled():
     per = w.chunk // w.group
     for h in range(w.Hq):
         assert sorted(set(g // per for g in gidx[0, h, -1])) == inp.planted[(0, h)]
+    # the prefill step the benchmark times (refresh of the new keys' chunks,
+    # routing, attention) against the sampled-and-checked separate calls
+    cm, gm = hga.build_summaries(out["K"], w.chunk, w.group)
+    O, lse, c_d, g_d = hga.decode_step_ex(out["Q"], out["K"], out["V"], cm, gm, w.T, w.chunk,
+                                          w.group, w.k_chunk, w.k_group)
+    torch.cuda.synchronize()
+    assert torch.equal(cm, out["cm"]) and torch.equal(gm, out["gm"])
+    assert torch.equal(g_d, out["gidx"]) and torch.equal(c_d, out["cidx"])
+    _same_attention(O, lse, out["O"], out["lse"], w.dtype)
 
 
 def test_host_tier_b4_t262144_sampled():
