@@ -237,8 +237,8 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
   float* gm_w = const_cast<float*>(gm);
   // Early refresh: when all the new keys lie in one chunk (always so in
   // decode), that chunk is every row's own chunk L, which is kept whatever its
-  // score, so level 1 needs nothing from the refresh. Each wave then issues the
-  // loads of one of its groups first (the lean form, which keeps to 128 VGPRs,
+  // score, so level 1 needs nothing from the refresh. Wave w then issues the
+  // key loads of that chunk's group w first (the lean form, which keeps to 128 VGPRs,
   // scores level 1 in smaller passes to leave room for them), they stay in
   // flight while level 1 scores the older chunks, and the waves fold them
   // while wave 0 ranks the chunks (wave 0 folds its own after). Same rows,
