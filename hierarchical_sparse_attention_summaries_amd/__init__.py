@@ -20,7 +20,8 @@ import torch
 __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summaries",
            "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
            "Layout", "build_summaries_ex", "update_summaries_ex", "route_ex", "attend_ex",
-           "route_fresh_ex",
+           "route_fresh_ex", "decode_step_ex", "decode_step_one_launch",
+           "decode_step_one_launch_cus", "workspace_check", "workspace_reset", "attend_staged",
            "LIB_PATH", "WORKSPACE_ZERO_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
@@ -28,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
 F32, BF16 = 0, 1
 _STATUS = {0: "HGA_OK", -1: "HGA_ERR_NULL", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_DTYPE",
            -4: "HGA_ERR_LAYOUT", -5: "HGA_ERR_PARAM", -6: "HGA_ERR_WORKSPACE",
-           -7: "HGA_ERR_HIP", -8: "HGA_ERR_UNSUPPORTED"}
+           -7: "HGA_ERR_HIP", -8: "HGA_ERR_UNSUPPORTED", -9: "HGA_ERR_TIMEOUT"}
+ERR_TIMEOUT = -9
 
 
 class HGAError(RuntimeError):
@@ -112,6 +114,10 @@ def _load():
         "hga_attend_staged": (ctypes.c_int, [P(Shape), vp, vp, vp, i32, vp, i32, i32, f32, vp, vp,
                                              vp, vp, i64, vp, sz, vp]),
         "hga_decode_step_one_launch": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, i32, P(i32)]),
+        "hga_decode_step_one_launch_cus": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, i32, i32,
+                                                          P(i32)]),
+        "hga_workspace_check": (ctypes.c_int, [vp, sz, vp]),
+        "hga_workspace_reset": (ctypes.c_int, [vp, sz, vp]),
         "hga_decode_step_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, vp, i32,
                                               i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
     }
@@ -439,12 +445,39 @@ def decode_step_one_launch(shape: Shape, dtype: str, chunk, group, k_chunk, k_gr
     return bool(one.value)
 
 
+def decode_step_one_launch_cus(shape: Shape, dtype: str, chunk, group, k_chunk, k_group,
+                               compute_units: int) -> bool:
+    """The same decision for a device of `compute_units` CUs (no device needed)."""
+    one = ctypes.c_int32()
+    code = {"f32": F32, "bf16": BF16}[dtype]
+    _check(_lib.hga_decode_step_one_launch_cus(ctypes.byref(shape), code, chunk, group, k_chunk,
+                                               k_group, compute_units, ctypes.byref(one)),
+           "hga_decode_step_one_launch_cus")
+    return bool(one.value)
+
+
+def workspace_check(workspace: torch.Tensor):
+    """Synchronises the current stream and raises HGAError(HGA_ERR_TIMEOUT) if
+    a bounded wait of a one-launch decode step on this workspace gave up (its
+    rows are NaN; the workspace stays flagged until workspace_reset)."""
+    _check(_lib.hga_workspace_check(_ptr(workspace), workspace.numel(),
+                                    _stream(workspace.device)), "hga_workspace_check")
+
+
+def workspace_reset(workspace: torch.Tensor):
+    """Zeroes the workspace's zero region (status word included), in stream order."""
+    _check(_lib.hga_workspace_reset(_ptr(workspace), workspace.numel(),
+                                    _stream(workspace.device)), "hga_workspace_reset")
+
+
 def decode_step_ex(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chunk, k_group,
                    layout=None, scale=0.0, want_chunks=True, want_lse=True, chunk_idx=None,
-                   group_idx=None, out=None, lse=None, workspace=None):
+                   group_idx=None, out=None, lse=None, workspace=None, check=False):
     """One decode step: refresh the summaries of each sequence's newest Nq keys
     from K, route, and attend (one launch for small batches). Returns
-    (O, lse, chunk_idx, group_idx)."""
+    (O, lse, chunk_idx, group_idx). With check=True the call synchronises and
+    raises HGAError(HGA_ERR_TIMEOUT) if a bounded wait gave up (see
+    workspace_check)."""
     _need(Q, "Q", 4)
     _need(K, "K", 4, host_ok=True)
     _need(V, "V", 4, host_ok=True)
@@ -469,6 +502,8 @@ def decode_step_ex(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chu
                                    _ptr(chunk_idx if want_chunks else None), _ptr(group_idx),
                                    _ptr(out), _ptr(lse if want_lse else None), _ptr(ws),
                                    ws.numel(), _stream(Q.device)), "hga_decode_step_ex")
+    if check:
+        workspace_check(ws)
     return out, (lse if want_lse else None), chunk_idx, group_idx
 
 

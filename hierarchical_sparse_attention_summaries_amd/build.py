@@ -10,6 +10,7 @@ linked into one shared library with a plain C ABI (include/hga.h).
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -28,6 +29,16 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+
+
+def header_abi_version() -> int:
+    """HGA_ABI_VERSION as include/hga.h defines it: the version a freshly built
+    library must report."""
+    with open(os.path.join(ROOT, "include", "hga.h")) as f:
+        m = re.search(r"^#define HGA_ABI_VERSION (\d+)\s*$", f.read(), flags=re.M)
+    if not m:
+        raise RuntimeError("include/hga.h defines no HGA_ABI_VERSION")
+    return int(m.group(1))
 
 
 def sources():

@@ -3,17 +3,60 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
 
 #include "hga.h"
 #include "hga_internal.h"
 
 namespace hga {
 
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0: not queried yet
+}  // namespace
+
 int device_cu_count() {
-  // Launch shapes are planned for MI355X/MI350X (gfx950): 256 CUs in 8 XCDs.
-  // Planning never queries the device, so size queries work without one.
-  return 256;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int known = g_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1)
+    return -1;
+  if (dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int resident_cu_count() {
+  // A CU mask restricts the CUs a process's queues may use, and the device
+  // attribute does not show it: then no launch may count on co-residency.
+  static const bool masked = std::getenv("HSA_CU_MASK") != nullptr ||
+                             std::getenv("ROC_GLOBAL_CU_MASK") != nullptr;
+  if (masked) return 0;
+  const int n = device_cu_count();
+  return n > 0 ? n : 0;
+}
+
+namespace {
+__global__ void zero_fill_kernel(uint4* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 16;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 1024));
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<uint4*>(p), n);
+  return hipGetLastError();
 }
 
 }  // namespace hga
@@ -140,11 +183,12 @@ bool row_fresh_fused(const hga_shape* s, int32_t dtype, int32_t chunk, int32_t g
            hga::use_prefill_route(dtype, s->q_heads, s->kv_heads, s->n_queries, s->head_dim));
 }
 
-// Whether hga_decode_step_ex runs as one launch (small batches).
+// Whether hga_decode_step_ex runs as one launch (small batches) on a device
+// whose workgroups can all hold `cus` compute units at once.
 bool decode_one_launch(const hga_shape* s, int32_t chunk, int32_t group, int32_t k_chunk,
-                       int32_t k_group) {
+                       int32_t k_group, int cus) {
   return hga::decode_step_one_launch(s->batch, s->q_heads, s->kv_heads, s->n_queries, s->seq_len,
-                                     s->head_dim, chunk, group, k_chunk, k_group);
+                                     s->head_dim, chunk, group, k_chunk, k_group, cus);
 }
 
 // Workspace of hga_decode_step_ex: the larger of the two-call form (routing,
@@ -202,6 +246,8 @@ const char* hga_status_str(int status) {
     case HGA_ERR_WORKSPACE: return "workspace too small";
     case HGA_ERR_HIP: return "HIP call or kernel launch failed";
     case HGA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case HGA_ERR_TIMEOUT:
+      return "a bounded wait inside a decode step gave up; its rows are NaN; reset the workspace";
     default: return "unknown status";
   }
 }
@@ -533,16 +579,49 @@ int hga_attend_staged(const hga_shape* shape, const void* Q, const void* K, cons
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 
+int hga_decode_step_one_launch_cus(const hga_shape* shape, int32_t dtype, int32_t chunk,
+                                   int32_t group, int32_t k_chunk, int32_t k_group,
+                                   int32_t compute_units, int32_t* one) {
+  int st = check_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!one) return HGA_ERR_NULL;
+  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
+  if (compute_units < 0) return HGA_ERR_PARAM;
+  st = check_route_params(shape, chunk, group, k_chunk, k_group);
+  if (st != HGA_OK) return st;
+  *one = decode_one_launch(shape, chunk, group, k_chunk, k_group, compute_units) ? 1 : 0;
+  return HGA_OK;
+}
+
 int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
                                int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one) {
   int st = check_shape(shape);
   if (st != HGA_OK) return st;
   if (!one) return HGA_ERR_NULL;
-  if (!dtype_ok(dtype)) return HGA_ERR_DTYPE;
-  st = check_route_params(shape, chunk, group, k_chunk, k_group);
-  if (st != HGA_OK) return st;
-  *one = decode_one_launch(shape, chunk, group, k_chunk, k_group) ? 1 : 0;
-  return HGA_OK;
+  if (hga::device_cu_count() < 1) return HGA_ERR_HIP;
+  return hga_decode_step_one_launch_cus(shape, dtype, chunk, group, k_chunk, k_group,
+                                        hga::resident_cu_count(), one);
+}
+
+int hga_workspace_check(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return HGA_ERR_NULL;
+  if (!aligned16(workspace)) return HGA_ERR_LAYOUT;
+  if (workspace_bytes < hga::kZeroBytes) return HGA_ERR_WORKSPACE;
+  if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return HGA_ERR_HIP;
+  int32_t word = 0;
+  if (hipMemcpy(&word, static_cast<const char*>(workspace) + hga::kStatusOffset, sizeof(word),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return HGA_ERR_HIP;
+  return word == 0 ? HGA_OK : HGA_ERR_TIMEOUT;
+}
+
+int hga_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return HGA_ERR_NULL;
+  if (!aligned16(workspace)) return HGA_ERR_LAYOUT;
+  if (workspace_bytes < hga::kZeroBytes) return HGA_ERR_WORKSPACE;
+  return hga::launch_zero_fill(workspace, hga::kZeroBytes, as_stream(stream)) == hipSuccess
+             ? HGA_OK
+             : HGA_ERR_HIP;
 }
 
 int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
@@ -567,7 +646,8 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   if (workspace_bytes < decode_workspace_bytes(shape, chunk, group, k_chunk, k_group))
     return HGA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  if (!decode_one_launch(shape, chunk, group, k_chunk, k_group)) {
+  const int cus = hga::resident_cu_count();
+  if (!decode_one_launch(shape, chunk, group, k_chunk, k_group, cus)) {
     // refresh + route, then attend
     st = hga_route_fresh_ex(shape, layout, Q, K, dtype, chunk_mean, group_mean, chunk, group,
                             k_chunk, k_group, scale, chunk_idx, group_idx, ws, workspace_bytes,
@@ -580,14 +660,14 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
                                                shape->n_queries, shape->seq_len, chunk, group,
                                                k_chunk, k_group);
   const int64_t rows = shape->batch * shape->q_heads * shape->n_queries;
-  const hga::AttendPlan aplan = hga::plan_decode_attend(rows, shape->head_dim, k_group);
+  const hga::AttendPlan aplan = hga::plan_decode_attend(rows, shape->head_dim, k_group, cus);
   hga::RouteArgs ra = route_args(shape, layout, Q, chunk_mean, group_mean, chunk, group, k_chunk,
                                  k_group, scale, chunk_idx, group_idx, ws, rplan);
   ra.K = K;
   ra.kv = L;
   hga::AttendArgs aa = attend_args(shape, L, Q, K, V, group_idx, k_group, group, scale, O, lse,
                                    ws, aplan);
-  const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ws, as_stream(stream));
+  const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ws, cus, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
 

@@ -45,7 +45,7 @@ AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves) {
   // Enough waves to keep every CU's memory pipe busy (each wave keeps two
   // groups in flight), no more: larger groups_per_wave means fewer partials
   // to merge and fewer workgroups bumping one arrival counter.
-  const int64_t target_waves = 4 * static_cast<int64_t>(device_cu_count());
+  const int64_t target_waves = 4 * static_cast<int64_t>(kPlanCus);
   int gpw = 1;
   while (gpw < 16 && rows * ((k_g + 2 * gpw - 1) / (2 * gpw)) >= target_waves) gpw *= 2;
   (void)G;

@@ -383,6 +383,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   __shared__ bool s_ok;
   const int bid = static_cast<int>(blockIdx.x);
   const int U = ra.B * ra.Hkv;
+  // The workspace's status word, loaded first and read only after the scoring
+  // item: non-zero if a wait of an earlier step on this workspace gave up.
+  const int32_t status0 = load_shared_i32(aa.status);
   __shared__ FreshRows<D> s_fr;
   if (bid < U * st.items) score_item<T, D>(ra, st, bid % U, bid / U, s_fr);
   const int rows = ra.B * ra.Hq * ra.Nq;
@@ -448,7 +451,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
         if (idx < total) s_dyn[idx < nc ? c0 + idx : ra.n_c + g0 + idx - nc] = handoff_float(v[k]);
       }
     }
-    if (!arrived) s_ok = false;
+    if (!arrived) {
+      s_ok = false;
+      store_shared_i32(aa.status, kStatusTimedOut);
+    }
   };
   // Level 1 (wave 0): chunk 0, chunk L and the k_chunk best between.
   auto level1 = [&]() -> int {
@@ -481,20 +487,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   }
   const int gf = min(cf * ra.gpc, n2);
   const bool early = p >= 0 && L - 1 < cf;
-  if (threadIdx.x == 0) s_ok = true;
+  // After a wait that gave up, late stores may have left words in the zero
+  // region: a step on such a workspace reads no word and poisons its rows
+  // (until the caller resets the workspace).
+  const bool stale = status0 != 0;
+  if (threadIdx.x == 0) s_ok = !stale;
   __syncthreads();
-  poll(0, cf, 0, gf, threadIdx.x, kThreads);
-  if (!early) poll(cf, n1, gf, n2, threadIdx.x, kThreads);
+  if (!stale) {
+    poll(0, cf, 0, gf, threadIdx.x, kThreads);
+    if (!early) poll(cf, n1, gf, n2, threadIdx.x, kThreads);
+  }
   __syncthreads();
   int n_kept = 0;
   if (early) {
     if (wave == 0) {
-      n_kept = level1();
-    } else {
+      if (!stale) n_kept = level1();
+    } else if (!stale) {
       poll(cf, n1, gf, n2, threadIdx.x - kWave, kThreads - kWave);
     }
     __syncthreads();
-  } else if (wave == 0 && p >= 0) {
+  } else if (wave == 0 && p >= 0 && !stale) {
     n_kept = level1();
   }
   const bool ok = s_ok;
@@ -546,8 +558,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
 
 // Scoring items per unit: as many as the grid holds (at least two: the refresh
 // and the older summaries). U * items <= the CU count (U <= CUs / 2).
-int step_items(int64_t units) {
-  const int64_t cus = device_cu_count();
+int step_items(int64_t units, int cus) {
   return static_cast<int>(std::max<int64_t>(2, cus / units));
 }
 
@@ -610,13 +621,13 @@ static StepWords step_words(int64_t rows, int64_t NS, int n_splits, int64_t D) {
   return w;
 }
 
-AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g) {
+AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g, int cus) {
   // The fewest groups per wave (8 waves per workgroup) that keep one
   // workgroup per (row, split) within one per CU.
   const int W = kWaves;
   int gpw = 1;
   while (gpw < k_g &&
-         (rows * ((k_g + W * gpw - 1) / (W * gpw)) > device_cu_count() ||
+         (rows * ((k_g + W * gpw - 1) / (W * gpw)) > cus ||
           (k_g + W * gpw - 1) / (W * gpw) > kAttendMaxSplits))
     gpw *= 2;
   AttendPlan pl{};
@@ -630,27 +641,26 @@ AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g) {
 }
 
 bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int64_t D,
-                            int C, int G, int k_c, int k_g) {
-  const int64_t cus = device_cu_count();
+                            int C, int G, int k_c, int k_g, int cus) {
   const int64_t rows = B * Hq * Nq, units = B * Hkv;
-  if (2 * units > cus) return false;
+  if (cus < 2 || 2 * units > cus) return false;
   if (Nq > C || C / G > rowroute::kFreshMaxGpc) return false;  // the refresh's LDS rows
-  const AttendPlan plan = plan_decode_attend(rows, D, k_g);
+  const AttendPlan plan = plan_decode_attend(rows, D, k_g, cus);
   if (rows * plan.n_splits > cus) return false;
   const int64_t n_c = (T + C - 1) / C, n_g = (T + G - 1) / G;
   // the score and partial words live in the workspace's zero-at-rest region
-  if (step_words(rows, n_c + n_g, plan.n_splits, D).end > kZeroBytes) return false;
+  if (step_words(rows, n_c + n_g, plan.n_splits, D).end > kStatusOffset) return false;
   const int64_t cap = std::min<int64_t>(k_c + 2, n_c);
   const size_t lds = static_cast<size_t>(n_c + n_g + cap + std::max(k_c, k_g) + k_g) * 4;
   return lds + step_static_lds(D) <= 160 * 1024;
 }
 
 size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int k_g) {
-  return plan_decode_attend(B * Hq * Nq, D, k_g).bytes;
+  return plan_decode_attend(B * Hq * Nq, D, k_g, kPlanCus).bytes;
 }
 
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
-                              int dtype, void* workspace, hipStream_t stream) {
+                              int dtype, void* workspace, int cus, hipStream_t stream) {
   const StepWords w = step_words(static_cast<int64_t>(ra.B) * ra.Hq * ra.Nq, ra.n_c + ra.n_g,
                                  plan.n_splits, ra.D);
   char* ws = static_cast<char*>(workspace);
@@ -658,7 +668,8 @@ hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const A
   st.scores = reinterpret_cast<int32_t*>(ws + w.scores);
   AttendArgs a2 = aa;
   a2.partials = reinterpret_cast<float*>(ws + w.partials);
-  st.items = step_items(static_cast<int64_t>(ra.B) * ra.Hkv);
+  a2.status = reinterpret_cast<int32_t*>(ws + kStatusOffset);
+  st.items = step_items(static_cast<int64_t>(ra.B) * ra.Hkv, cus);
   st.n_splits = plan.n_splits;
   st.groups_per_wave = plan.groups_per_wave;
   if (dtype == kF32)

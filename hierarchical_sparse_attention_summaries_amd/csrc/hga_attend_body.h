@@ -256,7 +256,8 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
         static_cast<uint16_t*>(a.O)[off] = static_cast<uint16_t>(bf16_bits(v));
       }
     }
-    if (a.lse && d == 0) a.lse[row] = Lx > 0.f ? (Mx + log2f(Lx)) * kLn2 : -INFINITY;
+    if (a.lse && d == 0)
+      a.lse[row] = timed_out ? __builtin_nanf("") : Lx > 0.f ? (Mx + log2f(Lx)) * kLn2 : -INFINITY;
   };
 
   if (n_splits == 1) {
@@ -310,7 +311,10 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
         if (idx < total) s_part[D + 2 + idx] = handoff_float(v[u]);
       }
     }
-    if (!arrived) s_last = false;
+    if (!arrived) {
+      s_last = false;
+      if (a.status) store_shared_i32(a.status, kStatusTimedOut);
+    }
     __syncthreads();
     if (!s_last) timed_out = true;
     // every other split has stored its partial, so is past the row's scores

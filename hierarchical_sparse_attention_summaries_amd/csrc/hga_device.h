@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hga {
 
 constexpr int kWave = 64;
@@ -183,12 +185,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Per-lane bit set over a lane's E selection items (bit e = item e*64 + lane):
+// 32 bits while E <= 32, 64 bits above.
+template <int E>
+using SelMask = typename std::conditional<(E > 32), uint64_t, uint32_t>::type;
+static_assert(sizeof(SelMask<64>) * 8 >= 64, "one bit per item");
+
 // Top-k over the items of one wave. Item e*64 + lane holds key[e] (0 = absent).
 // Chooses the k largest keys, equal keys going to the lower item index; returns
 // a per-lane bit set (bit e = item e*64+lane chosen). Requires that more than
 // k items be present. All lanes of the wave must call it.
 template <int E>
-__device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) {
+__device__ __forceinline__ SelMask<E> wave_top_k(const uint32_t (&key)[E], int k) {
   // The k-th largest key is the largest t with #(key >= t) >= k; it is found
   // two bits per step from the top (the three candidate digits are counted
   // independently; the threshold stays in scalar registers). Stop early once
@@ -232,14 +240,14 @@ __device__ __forceinline__ uint32_t wave_top_k(const uint32_t (&key)[E], int k) 
   for (int e = 0; e < E; ++e) above += __popcll(ballot(key[e] > thr));
   const int need = k - above;  // keys equal to thr still to take, lowest index first
                                // (all of them after an early stop)
-  uint32_t chosen = 0;
+  SelMask<E> chosen = 0;
   int eq_before = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool eq = key[e] == thr;
     const uint64_t eqm = ballot(eq);
     const bool take = key[e] > thr || (eq && eq_before + bits_below(eqm) < need);
-    chosen |= static_cast<uint32_t>(take) << e;
+    chosen |= static_cast<SelMask<E>>(take) << e;
     eq_before += __popcll(eqm);
   }
   return chosen;

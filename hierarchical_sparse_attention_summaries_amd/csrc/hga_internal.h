@@ -19,6 +19,18 @@ constexpr int kBF16 = 1;
 constexpr size_t kCounterBytes = 65536;
 constexpr int kMaxCounters = static_cast<int>(kCounterBytes / sizeof(unsigned));
 constexpr size_t kZeroBytes = size_t{4} << 20;
+// The zero region's last 256 bytes hold the workspace's status word: zero
+// while every bounded wait of the one-launch decode step has completed; a
+// wait that gave up sets kStatusTimedOut, and the word stays set (every later
+// decode step on the workspace then reads no hand-off word and poisons its
+// rows) until the caller resets the workspace. Hand-off words end before it.
+constexpr size_t kStatusOffset = kZeroBytes - 256;
+constexpr int32_t kStatusTimedOut = 1;
+
+// Launch shapes that only tune speed (split counts, grid sizes of kernels
+// that never wait for one another) are planned for MI355X/MI350X: 256 CUs in
+// 8 XCDs, with no device query, so that size queries work without a device.
+constexpr int kPlanCus = 256;
 
 // Largest number of items one wave selects from (middle chunks, or candidate
 // groups of the kept chunks), and of chunks one query keeps.
@@ -121,6 +133,7 @@ struct AttendPlan {
 AttendPlan plan_attend(int64_t rows, int64_t D, int G, int k_g, int waves = 4);
 
 struct AttendArgs {
+  int32_t* status;     // the workspace's status word (one-launch decode step), or null
   const void* Q;
   const void* K;
   const void* V;
@@ -149,18 +162,19 @@ hipError_t launch_attend_tiles(const AttendArgs& a, hipStream_t stream);
 // attends for one (row, split). The scores [rows, n_c + n_g] and the splits'
 // partial sums travel as hand-off words in the workspace's zero-at-rest
 // region after the counters; no counter is used.
-// Attention plan inside the one-launch decode step (8 waves per workgroup).
-AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g);
-// Whether the one-launch form applies: the grid fits one workgroup per CU,
-// the refresh touches at most two chunks of at most 16 groups, the step's
-// hand-off words fit the zero-at-rest region, and the row's scores and
-// selection fit the LDS.
+// Attention plan inside the one-launch decode step (8 waves per workgroup) on
+// a device of `cus` compute units.
+AttendPlan plan_decode_attend(int64_t rows, int64_t D, int k_g, int cus);
+// Whether the one-launch form applies on a device of `cus` compute units: the
+// grid fits one workgroup per CU, the refresh touches at most two chunks of
+// at most 16 groups, the step's hand-off words fit the zero-at-rest region,
+// and the row's scores and selection fit the LDS.
 bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, int64_t D,
-                            int C, int G, int k_c, int k_g);
+                            int C, int G, int k_c, int k_g, int cus);
 // Workspace bytes of the one-launch form.
 size_t decode_step_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int k_g);
 hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const AttendPlan& plan,
-                              int dtype, void* workspace, hipStream_t stream);
+                              int dtype, void* workspace, int cus, hipStream_t stream);
 
 // Host-memory tier: the routed groups of each (sequence, KV head), over all
 // its query rows, copied once into a device pool of [pool_pages, G, D] pages;
@@ -188,6 +202,16 @@ struct StageArgs {
 };
 hipError_t launch_stage(const StageArgs& a, int dtype, hipStream_t stream);
 
+// Compute units of the current device (queried once per device), or -1 if
+// there is no device or it cannot be queried.
 int device_cu_count();
+// Compute units every workgroup of one launch may count on holding at once:
+// the device's, or 0 when a CU mask in the environment (HSA_CU_MASK,
+// ROC_GLOBAL_CU_MASK) may hide some of them from this process's queues.
+int resident_cu_count();
+
+// Zero-fills `bytes` bytes (a multiple of 16, 16-byte aligned) with a kernel
+// (no memset node, so it can be captured in a graph).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace hga

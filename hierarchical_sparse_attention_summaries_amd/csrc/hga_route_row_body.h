@@ -110,10 +110,10 @@ __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out
     const int i = e * kWave + lane;
     key[e] = i < n ? order_key(score(i)) : 0u;
   }
-  uint32_t chosen = 0;
+  SelMask<E> chosen = 0;
   if (n <= k) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) chosen |= static_cast<uint32_t>(key[e] != 0u) << e;
+    for (int e = 0; e < E; ++e) chosen |= static_cast<SelMask<E>>(key[e] != 0u) << e;
   } else {
     chosen = wave_top_k<E>(key, k);
   }

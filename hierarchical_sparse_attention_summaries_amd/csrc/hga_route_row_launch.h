@@ -54,7 +54,7 @@ template <bool FRESH>
 hipError_t launch_rows(const RouteArgs& a, int dtype, hipStream_t stream) {
   // One workgroup per CU at most: the big form (more registers, fewer memory
   // round trips); else the lean form, two workgroups per CU.
-  const bool big = route_row_grid(a) <= device_cu_count();
+  const bool big = route_row_grid(a) <= kPlanCus;
   if (dtype == kF32) {
     if (a.D == 64)
       return big ? launch_rows_t<float, 64, FRESH, true>(a, stream)

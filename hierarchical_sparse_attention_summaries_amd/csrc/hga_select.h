@@ -48,7 +48,7 @@ __device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, i
         const int t = e * kWave + lane;
         key[e] = t < L - 1 ? order_key(load_shared(cs + 1 + t)) : 0u;
       }
-      const uint32_t chosen = wave_top_k<E>(key, a.k_c);
+      const SelMask<E> chosen = wave_top_k<E>(key, a.k_c);
       int before = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -82,10 +82,10 @@ __device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, i
     key[e] = valid ? order_key(load_shared(gs + g)) : 0u;
     n_valid += __popcll(ballot(valid));
   }
-  uint32_t chosen = 0;
+  SelMask<E> chosen = 0;
   if (n_valid <= a.k_g) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) chosen |= static_cast<uint32_t>(key[e] != 0u) << e;
+    for (int e = 0; e < E; ++e) chosen |= static_cast<SelMask<E>>(key[e] != 0u) << e;
   } else {
     chosen = wave_top_k<E>(key, a.k_g);
   }

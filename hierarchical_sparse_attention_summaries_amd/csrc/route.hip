@@ -212,7 +212,7 @@ RoutePlan plan_route(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t T, 
   // most 768 summary rows per workgroup (their scores for 16 query rows are
   // staged in 48 KiB of LDS).
   const int64_t units = B * Hkv * pl.n_qblocks;
-  const int64_t target = static_cast<int64_t>(device_cu_count());
+  const int64_t target = static_cast<int64_t>(kPlanCus);
   int64_t splits = (target + units - 1) / units;
   const int64_t gpc = C / G;
   int64_t max_cps = 768 / (1 + gpc);

@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
             const int u = e * kWave + lane;
             key[e] = u < L - 1 ? order_key(cs[1 + u]) : 0u;
           }
-          const uint32_t chosen = wave_top_k<E>(key, a.k_c);
+          const SelMask<E> chosen = wave_top_k<E>(key, a.k_c);
           int before = 0;
 #pragma unroll
           for (int e = 0; e < E; ++e) {
@@ -447,10 +447,10 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
       const int u = e * kWave + lane;
       key[e] = u < n_valid ? order_key(gs[u]) : 0u;
     }
-    uint32_t chosen = 0;
+    SelMask<E> chosen = 0;
     if (n_valid <= a.k_g) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) chosen |= static_cast<uint32_t>(key[e] != 0u) << e;
+      for (int e = 0; e < E; ++e) chosen |= static_cast<SelMask<E>>(key[e] != 0u) << e;
     } else {
       chosen = wave_top_k<E>(key, a.k_g);
     }

@@ -32,13 +32,15 @@
  *     synchronisation, as usual for HIP. Nothing throws, prints or aborts.
  *   - Inputs must be finite (no NaN/Inf in Q, K, V).
  *   - Workspaces: the first hga_workspace_zero_bytes() bytes (4 MiB) of a
- *     workspace hold arrival counters and hand-off words and must be zero
- *     before the workspace's first use (e.g. allocate it zeroed). Every call
- *     leaves them at zero, so one workspace (large enough for each call) can
- *     serve calls of any shape in turn. Calls that may run concurrently must
- *     not share a workspace. After a call that returned HGA_ERR_HIP, or whose
- *     kernels faulted, the region's contents are unspecified: zero it again
- *     before the workspace's next use.
+ *     workspace hold arrival counters, hand-off words and (in the last 256
+ *     bytes) a status word, and must be zero before the workspace's first use
+ *     (e.g. allocate it zeroed, or call hga_workspace_reset). Every call leaves
+ *     them at zero, so one workspace (large enough for each call) can serve
+ *     calls of any shape in turn. Calls that may run concurrently must not
+ *     share a workspace. After a call that returned HGA_ERR_HIP, whose kernels
+ *     faulted, or after which hga_workspace_check returns HGA_ERR_TIMEOUT, the
+ *     region's contents are unspecified: reset it before the workspace's next
+ *     use.
  */
 #ifndef HGA_H
 #define HGA_H
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 2
+#define HGA_ABI_VERSION 3
 
 typedef enum hga_status {
   HGA_OK = 0,
@@ -61,7 +63,9 @@ typedef enum hga_status {
   HGA_ERR_PARAM = -5,       /* chunk/group/k_chunk/k_group/range out of range */
   HGA_ERR_WORKSPACE = -6,   /* workspace smaller than the size query says */
   HGA_ERR_HIP = -7,         /* a HIP call or kernel launch failed */
-  HGA_ERR_UNSUPPORTED = -8  /* a valid request this build has no kernel for */
+  HGA_ERR_UNSUPPORTED = -8, /* a valid request this build has no kernel for */
+  HGA_ERR_TIMEOUT = -9      /* hga_workspace_check: a bounded wait inside a one-launch decode
+                               step on this workspace gave up (its rows were poisoned) */
 } hga_status;
 
 typedef enum hga_dtype {
@@ -279,11 +283,40 @@ int hga_attend_staged(const hga_shape* shape, const void* Q, const void* K, cons
 int hga_decode_step_workspace_size(const hga_shape* shape, int32_t chunk, int32_t group,
                                    int32_t k_chunk, int32_t k_group, size_t* bytes);
 
-/* Whether hga_decode_step_ex runs these arguments as one launch: *one = 1,
- * else 0 (the calls it then enqueues are hga_route_fresh_ex and
- * hga_attend_ex). */
+/* Whether hga_decode_step_ex runs these arguments as one launch on the
+ * current device: *one = 1, else 0 (the calls it then enqueues are
+ * hga_route_fresh_ex and hga_attend_ex). The one-launch form needs every one
+ * of its workgroups resident at once, one per compute unit: it is chosen only
+ * when the grid fits the device's compute units (queried once per device),
+ * and never when a CU mask (HSA_CU_MASK or ROC_GLOBAL_CU_MASK) is set in the
+ * environment. HGA_ERR_HIP if there is no current device. */
 int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t chunk,
                                int32_t group, int32_t k_chunk, int32_t k_group, int32_t* one);
+
+/* The same decision for a device whose workgroups can hold `compute_units`
+ * compute units at once (>= 0; 0: never one launch). Needs no device. */
+int hga_decode_step_one_launch_cus(const hga_shape* shape, int32_t dtype, int32_t chunk,
+                                   int32_t group, int32_t k_chunk, int32_t k_group,
+                                   int32_t compute_units, int32_t* one);
+
+/*
+ * Status of a workspace after the work enqueued on `stream`: synchronises the
+ * stream, then reads the workspace's status word. HGA_OK if every bounded wait
+ * of the one-launch decode steps on it completed; HGA_ERR_TIMEOUT if one gave
+ * up (its rows got NaN in O and lse and -1 ids). The flag is sticky: until the
+ * workspace is reset, every later one-launch decode step on it reads no
+ * hand-off word (late stores of the step that gave up may have left some) and
+ * poisons its rows the same way, while still refreshing the summaries.
+ * Waits give up only if the step's workgroups are not all resident at once
+ * (a concurrent kernel holding compute units the step was planned for).
+ * workspace_bytes >= hga_workspace_zero_bytes(). Not for use during stream
+ * capture (it synchronises).
+ */
+int hga_workspace_check(const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Zeroes the workspace's zero region (status word included) on `stream`, with
+ * a kernel (no memset, so the call can be captured in a graph). */
+int hga_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One decode step, all three HGA steps (abstract: summaries, routing by
@@ -302,11 +335,12 @@ int hga_decode_step_one_launch(const hga_shape* shape, int32_t dtype, int32_t ch
  * share of one KV head's summaries against all of its query rows and writes
  * the scores into the zero region as words that are never zero; then it polls
  * its own row's words until all have arrived (a bounded wait; a row whose
- * scores do not all arrive in time gets NaN in O and lse, and the zero region
- * must then be zeroed again before the workspace's next use), selects, and
+ * scores do not all arrive in time gets NaN in O and lse and -1 ids, and the
+ * workspace's status word records it: see hga_workspace_check), selects, and
  * attends to its share of the row's groups. The workgroup that finishes a row
  * zeroes the row's words. Otherwise the two calls are enqueued. Calls that
- * share a workspace must not overlap.
+ * share a workspace must not overlap, and no other kernel should hold the
+ * device's compute units while a one-launch step runs.
  */
 int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
                        const void* K, const void* V, int32_t dtype, float* chunk_mean,

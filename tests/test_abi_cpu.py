@@ -12,7 +12,18 @@ import hierarchical_sparse_attention_summaries_amd as hga
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hga.h")
 
-OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED, TIMEOUT = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+def _build_script():
+    """The build script, loaded by path (as __graft_entry__.build() loads it)."""
+    import importlib.util
+    path = os.path.join(ROOT, "hierarchical_sparse_attention_summaries_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("hga_build_script_test", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def declared_functions():
@@ -31,10 +42,45 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_text():
     L = hga.lib()
-    assert L.hga_abi_version() == 2
+    # the check __graft_entry__.build() makes after building
+    assert L.hga_abi_version() == _build_script().header_abi_version() == 3
     assert hga.WORKSPACE_ZERO_BYTES == 4 << 20
-    for s in (OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED, 123):
+    for s in (OK, NULL, SHAPE, DTYPE, LAYOUT, PARAM, WORKSPACE, HIP, UNSUPPORTED, TIMEOUT, 123):
         assert len(L.hga_status_str(s)) > 0
+    assert b"reset" in L.hga_status_str(TIMEOUT)
+
+
+def test_decode_step_planner_follows_the_compute_units():
+    """The one-launch decode step needs all of its workgroups resident at once
+    (one per CU): the planner takes it only when the grid fits the CUs."""
+    s = _shape()                                  # batch 1, 32 query rows, 64K context
+    one = lambda cus, sh=s: hga.decode_step_one_launch_cus(sh, "bf16", 256, 32, 32, 64, cus)
+    assert one(256)                               # 8 attention workgroups per row
+    assert one(128)                               # 4 per row, 8 groups per wave
+    assert one(32)                                # 1 per row: 32 workgroups
+    assert not one(31)                            # 32 rows cannot be resident on 31 CUs
+    assert not one(0)                             # no co-residency (e.g. a CU mask)
+    assert not one(7, _shape(batch=4))            # 2 * 16 scoring units > 7
+    b16 = _shape(batch=16)
+    assert not one(256, b16)                      # 512 rows: more workgroups than CUs
+    # 512 rows would fit 1024 CUs, but their score words exceed the zero region
+    assert not one(1024, b16)
+    L = hga.lib()
+    o = ctypes.c_int32()
+    f = L.hga_decode_step_one_launch_cus
+    assert f(ctypes.byref(s), 1, 256, 32, 32, 64, -1, ctypes.byref(o)) == PARAM
+    assert f(ctypes.byref(s), 1, 256, 32, 32, 64, 256, None) == NULL
+    assert f(ctypes.byref(s), 7, 256, 32, 32, 64, 256, ctypes.byref(o)) == DTYPE
+    assert f(None, 1, 256, 32, 32, 64, 256, ctypes.byref(o)) == NULL
+
+
+def test_workspace_check_and_reset_reject_before_any_device_call():
+    L = hga.lib()
+    Z = hga.WORKSPACE_ZERO_BYTES
+    for f in (L.hga_workspace_check, L.hga_workspace_reset):
+        assert f(None, Z, None) == NULL
+        assert f(MIS, Z, None) == LAYOUT
+        assert f(FAKE, Z - 1, None) == WORKSPACE
 
 
 def test_summary_counts():

@@ -143,13 +143,16 @@ def test_prefill_4096_on_61440_sampled():
 
 def test_host_tier_b4_t262144_sampled():
     """Full K/V in pinned host memory, summaries in HBM: the routed groups are
-    read over the host link. 256 sampled query rows against the oracle."""
+    read over the host link. Every one of the workload's 128 query rows
+    against the oracle (the per-row oracle path of the sampled check)."""
     w = HOST_TIER
     log(f"case {w.name}")
     inp = generate(w)
     out = run_hip(w, inp)
     assert not out["K"].is_cuda and out["cm"].is_cuda
-    check_sampled(w, inp, out, n_rows=128)
+    rows = w.B * w.Hq * w.Nq
+    st, _ = check_sampled(w, inp, out, n_rows=rows)
+    assert st.queries == rows == 128
 
 
 @pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
@@ -177,20 +180,20 @@ def test_qwen3_decode_64k():
 
 @pytest.mark.parametrize("T", sorted(SWEEP))
 def test_sweep_b16(T):
+    """Every sequence of the batch-16 sweep point: the decode step the
+    benchmark times (refreshing route, then attention) against the oracle
+    element by element, and the three separate calls against the decode step
+    (summaries and routes bit for bit, attention to fp32 rounding)."""
     w = SWEEP[T]
     log(f"case {w.name}")
     inp = generate(w)
     out = run_hip(w, inp)
-    b_list = None if T <= 16384 else [0, 7, 15]
-    check_workload(w, inp, out, b_list=b_list)
-    # the decode step the benchmark times at batch 16 (refreshing route, then
-    # attention) against the separate calls checked above: summaries and routes
-    # bit for bit, attention to fp32 rounding
-    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    Q, K, V = out["Q"], out["K"], out["V"]
     cm, gm = hga.build_summaries(K, w.chunk, w.group)
     O, lse, c_d, g_d = hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk,
                                           w.k_group)
     torch.cuda.synchronize()
+    check_workload(w, inp, dict(cm=cm, gm=gm, cidx=c_d, gidx=g_d, O=O, lse=lse))
     assert torch.equal(cm, out["cm"]) and torch.equal(gm, out["gm"])
     assert torch.equal(g_d, out["gidx"]) and torch.equal(c_d, out["cidx"])
     _same_attention(O, lse, out["O"], out["lse"], w.dtype)
@@ -562,10 +565,94 @@ def test_decode_step_equals_fresh_route_then_attend(case):
     assert torch.equal(cm_d, cm_r) and torch.equal(gm_d, gm_r)
     _zero_regions_are_zero()
     _same_attention(O_d, lse_d, O_r, lse_r, w.dtype)
-    if layout is None and w.T <= 8192:
-        from synth.inputs import Inputs
+    # the step's own outputs against the oracle on the modified keys
+    from synth.inputs import Inputs
+    if layout is None:
         inp2 = Inputs(w, inp.seed, inp.Q, Kc.float().cpu().numpy(), inp.V)
         check_workload(w, inp2, dict(cm=cm_d, gm=gm_d, cidx=c_d, gidx=g_d, O=O_d, lse=lse_d))
+    else:
+        # the logical dense cache with the same bf16 update of each newest key
+        Kd = torch.from_numpy(inp.K).to(torch.bfloat16)
+        for b, Tb in enumerate(info[0]):
+            Kd[b, :, Tb - w.Nq:Tb] += 0.75
+        inp2 = Inputs(w, inp.seed, inp.Q, Kd.float().numpy(), inp.V)
+        from tests.gpu_runner import check_ragged
+        check_ragged(w, inp2, info[0], dict(cm=cm_d, gm=gm_d, cidx=c_d, gidx=g_d, O=O_d,
+                                            lse=lse_d))
+
+
+# More than 2048 items for one wave to select from (4094 middle chunks: 64 keys
+# per lane), through every routing form: the row route, the refreshing row
+# route, the one-launch decode step, and the MFMA prefill route's select
+# kernel (16 queries per head).
+WIDE = DECODE_64K.with_(name="wide-c16-g8-t65536", Hq=4, Hkv=1, chunk=16, group=8, k_chunk=64,
+                        k_group=32, plants=4)
+
+
+@pytest.mark.parametrize("Nq", [1, 16])
+def test_select_over_4094_chunks(Nq):
+    w = WIDE.with_(Nq=Nq)
+    log(f"case {w.name} Nq={Nq}")
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+    Q, K, V = out["Q"], out["K"], out["V"]
+    cm, gm = out["cm"].clone(), out["gm"].clone()
+    c_f, g_f = hga.route_fresh_ex(Q, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
+    torch.cuda.synchronize()
+    assert torch.equal(c_f, out["cidx"]) and torch.equal(g_f, out["gidx"])
+    if Nq == 1:
+        assert hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+    cm2, gm2 = out["cm"].clone(), out["gm"].clone()
+    O, lse, c_d, g_d = hga.decode_step_ex(Q, K, V, cm2, gm2, w.T, w.chunk, w.group, w.k_chunk,
+                                          w.k_group, check=True)
+    torch.cuda.synchronize()
+    check_workload(w, inp, dict(cm=cm2, gm=gm2, cidx=c_d, gidx=g_d, O=O, lse=lse))
+    assert torch.equal(c_d, out["cidx"]) and torch.equal(g_d, out["gidx"])
+
+
+def test_decode_step_status_word_is_sticky_until_reset():
+    """A workspace whose status word says an earlier wait gave up: the next
+    one-launch decode step reads no hand-off word and poisons every row (NaN
+    O and lse, -1 ids) while still refreshing the summaries; the check reports
+    HGA_ERR_TIMEOUT until the workspace is reset, after which the step is
+    exact again. (The flag is set from the host: no kernel waits in vain.)"""
+    w = DECODE_64K.with_(B=2, T=8192, k_chunk=4, k_group=8, plants=2)
+    log("case decode-step-status-word")
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    assert hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    cm0, gm0 = hga.build_summaries(K, w.chunk, w.group)
+    K[:, :, -1] += 0.75            # the newest key changed after the summaries were built
+    nbytes = hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk, w.k_group)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    Z = hga.WORKSPACE_ZERO_BYTES
+
+    def step(check):
+        cm, gm = cm0.clone(), gm0.clone()
+        res = hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                                 workspace=ws, check=check)
+        torch.cuda.synchronize()
+        return res, cm, gm
+
+    (O, lse, c, g), cm, gm = step(True)
+    ws[Z - 256:Z - 252] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    (O2, lse2, c2, g2), cm2, gm2 = step(False)
+    assert bool(torch.isnan(O2.float()).all()) and bool(torch.isnan(lse2).all())
+    assert bool((g2 == -1).all()) and bool((c2 == -1).all())
+    assert torch.equal(cm2, cm) and torch.equal(gm2, gm)
+    with pytest.raises(hga.HGAError) as err:
+        hga.workspace_check(ws)
+    assert err.value.status == hga.ERR_TIMEOUT
+    hga.workspace_reset(ws)
+    hga.workspace_check(ws)
+    assert int(ws[:Z].count_nonzero()) == 0
+    (O3, lse3, c3, g3), _, _ = step(True)
+    assert torch.equal(O3, O) and torch.equal(lse3, lse)
+    assert torch.equal(c3, c) and torch.equal(g3, g)
+    assert int(ws[:Z].count_nonzero()) == 0
 
 
 def test_decode_step_one_launch_ragged_short_and_empty():
