@@ -21,7 +21,7 @@ __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summa
            "route", "attend", "route_workspace_bytes", "attend_workspace_bytes", "Shape",
            "Layout", "build_summaries_ex", "update_summaries_ex", "route_ex", "attend_ex",
            "route_fresh_ex", "decode_step_ex", "decode_step_one_launch",
-           "decode_step_one_launch_cus", "workspace_check", "workspace_reset", "attend_staged",
+           "decode_step_one_launch_cus", "workspace_check", "workspace_reset", "attend_staged", "decode_step_noalloc",
            "LIB_PATH", "WORKSPACE_ZERO_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
@@ -117,6 +117,9 @@ def _load():
         "hga_decode_step_one_launch_cus": (ctypes.c_int, [P(Shape), i32, i32, i32, i32, i32, i32,
                                                           P(i32)]),
         "hga_workspace_check": (ctypes.c_int, [vp, sz, vp]),
+        "hga_decode_step_noalloc": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp,
+                                                   vp, i32, i32, i32, i32, f32, vp, vp, vp, vp,
+                                                   i32, vp]),
         "hga_workspace_reset": (ctypes.c_int, [vp, sz, vp]),
         "hga_decode_step_ex": (ctypes.c_int, [P(Shape), P(_KvLayoutC), vp, vp, vp, i32, vp, vp, i32,
                                               i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
@@ -504,6 +507,40 @@ def decode_step_ex(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chu
                                    ws.numel(), _stream(Q.device)), "hga_decode_step_ex")
     if check:
         workspace_check(ws)
+    return out, (lse if want_lse else None), chunk_idx, group_idx
+
+
+def decode_step_noalloc(Q, K, V, chunk_mean, group_mean, seq_len, chunk, group, k_chunk,
+                        k_group, layout=None, scale=0.0, want_chunks=True, want_lse=True,
+                        chunk_idx=None, group_idx=None, out=None, lse=None, reset=False):
+    """decode_step_ex whose scratch is the library's fixed per-device array (no
+    workspace; the library call allocates nothing; outputs given as out=,
+    lse=, group_idx=, chunk_idx= are used as they are). reset=True clears the
+    array's zero region first (after NaN rows from a wait that gave up).
+    Returns (O, lse, chunk_idx, group_idx)."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, host_ok=True)
+    _need(V, "V", 4, host_ok=True)
+    B, Hq, Nq, D = Q.shape
+    Hkv = chunk_mean.shape[1]
+    if tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K and V differ in shape")
+    shape = _shape(Q, Hkv, seq_len)
+    if want_chunks and chunk_idx is None:
+        chunk_idx = torch.empty((B, Hq, Nq, k_chunk + 2), dtype=torch.int32, device=Q.device)
+    if group_idx is None:
+        group_idx = torch.empty((B, Hq, Nq, k_group), dtype=torch.int32, device=Q.device)
+    if out is None:
+        out = torch.empty_like(Q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    _check(_lib.hga_decode_step_noalloc(ctypes.byref(shape), _lay(layout), _ptr(Q), _ptr(K),
+                                        _ptr(V), _dtype_code(Q), _ptr(chunk_mean),
+                                        _ptr(group_mean), chunk, group, k_chunk, k_group,
+                                        float(scale), _ptr(chunk_idx if want_chunks else None),
+                                        _ptr(group_idx), _ptr(out),
+                                        _ptr(lse if want_lse else None), 1 if reset else 0,
+                                        _stream(Q.device)), "hga_decode_step_noalloc")
     return out, (lse if want_lse else None), chunk_idx, group_idx
 
 

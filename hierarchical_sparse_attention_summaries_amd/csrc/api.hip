@@ -630,6 +630,19 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
                        int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
                        void* O, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream) {
+  return hga::decode_step_call(shape, layout, Q, K, V, dtype, chunk_mean, group_mean, chunk,
+                               group, k_chunk, k_group, scale, chunk_idx, group_idx, O, lse,
+                               workspace, workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+int hga::decode_step_call(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                          const void* K, const void* V, int32_t dtype, float* chunk_mean,
+                          float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+                          int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+                          void* O, float* lse, void* workspace, size_t workspace_bytes,
+                          bool clear_first, void* stream) {
   int st = check_shape(shape);
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !chunk_mean || !group_mean || !group_idx || !O || !workspace)
@@ -646,6 +659,9 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   if (workspace_bytes < decode_workspace_bytes(shape, chunk, group, k_chunk, k_group))
     return HGA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
+  // every argument is valid: from here on the call enqueues work
+  if (clear_first && hga::launch_zero_fill(ws, hga::kZeroBytes, as_stream(stream)) != hipSuccess)
+    return HGA_ERR_HIP;
   const int cus = hga::resident_cu_count();
   if (!decode_one_launch(shape, chunk, group, k_chunk, k_group, cus)) {
     // refresh + route, then attend
@@ -670,5 +686,3 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
   const hipError_t e = hga::launch_decode_step(ra, aa, aplan, dtype, ws, cus, as_stream(stream));
   return e == hipSuccess ? HGA_OK : HGA_ERR_HIP;
 }
-
-}  // extern "C"

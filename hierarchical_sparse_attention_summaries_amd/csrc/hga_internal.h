@@ -210,6 +210,21 @@ int device_cu_count();
 // ROC_GLOBAL_CU_MASK) may hide some of them from this process's queues.
 int resident_cu_count();
 
+}  // namespace hga
+
+#include "hga.h"
+
+namespace hga {
+
+// hga_decode_step_ex with an optional clear of the workspace's zero region
+// (enqueued first, once every argument has been checked).
+int decode_step_call(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                     const void* K, const void* V, int32_t dtype, float* chunk_mean,
+                     float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+                     int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+                     void* O, float* lse, void* workspace, size_t workspace_bytes,
+                     bool clear_first, void* stream);
+
 // Zero-fills `bytes` bytes (a multiple of 16, 16-byte aligned) with a kernel
 // (no memset node, so it can be captured in a graph).
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);

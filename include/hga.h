@@ -349,6 +349,30 @@ int hga_decode_step_ex(const hga_shape* shape, const hga_kv_layout* layout, cons
                        void* O, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * hga_decode_step_ex for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, with the same results, whose scratch is a fixed
+ * 16 MiB array in the library's own device memory instead of a caller
+ * workspace. The call allocates nothing.
+ *   Arguments as hga_decode_step_ex, without workspace and workspace_bytes.
+ *   reset      non-zero: clear the scratch's zero region first (in stream
+ *              order), as after a step whose bounded wait gave up (its rows
+ *              NaN; every later step on the scratch stays poisoned until a
+ *              reset). The first call on each device clears it by itself.
+ * HGA_ERR_WORKSPACE if the step needs more scratch than the array holds
+ * (hga_decode_step_workspace_size > 16 MiB; e.g. more than 42 sequences at a
+ * 64K context with 32 query heads): use hga_decode_step_ex then. Each device
+ * the library runs on holds its own array until the process ends. Every call
+ * on one device shares that device's array, which keeps the last call's
+ * contents: calls that overlap on one device (other streams or threads) race.
+ */
+int hga_decode_step_noalloc(const hga_shape* shape, const hga_kv_layout* layout, const void* Q,
+                            const void* K, const void* V, int32_t dtype, float* chunk_mean,
+                            float* group_mean, int32_t chunk, int32_t group, int32_t k_chunk,
+                            int32_t k_group, float scale, int32_t* chunk_idx, int32_t* group_idx,
+                            void* O, float* lse, int32_t reset, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -231,6 +231,29 @@ def test_decode_step_rejects_before_launch():
     assert d(None, *args) == NULL
 
 
+def test_decode_step_noalloc_rejects_before_any_device_call():
+    """The allocation-free decode step refuses a step whose scratch would not
+    fit the library's fixed 16 MiB array (43 sequences at 64K), and bad
+    arguments, before it touches a device."""
+    L = hga.lib()
+    f = L.hga_decode_step_noalloc
+    # shape, layout, Q, K, V, dtype, cm, gm, chunk, group, k_chunk, k_group, scale,
+    # chunk_idx, group_idx, O, lse, reset, stream
+    args = [None, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 256, 32, 32, 64, ctypes.c_float(0.0), FAKE,
+            FAKE, FAKE, None, 0, None]
+    n = ctypes.c_size_t()
+    fits, too_big = _shape(batch=42), _shape(batch=43)
+    for s, ok in ((fits, True), (too_big, False)):
+        assert L.hga_decode_step_workspace_size(ctypes.byref(s), 256, 32, 32, 64,
+                                                ctypes.byref(n)) == OK
+        assert (n.value <= 16 << 20) == ok
+    assert f(ctypes.byref(too_big), *args) == WORKSPACE
+    assert f(None, *args) == NULL
+    bad = list(args); bad[10] = 0
+    assert f(ctypes.byref(fits), *bad) == PARAM          # k_group < 1
+    assert f(ctypes.byref(_shape(head_dim=96)), *args) == SHAPE
+
+
 def test_attend_staged_rejects_before_launch():
     L = hga.lib()
     pages, n = ctypes.c_int64(), ctypes.c_size_t()
