@@ -112,6 +112,12 @@ def main():
     from synth import ALL
 
     w = ALL[args.workload]
+    # The CPU oracle runs first, in forked worker processes, before anything
+    # touches the GPU (the workers inherit no GPU state and are gone before it
+    # is initialised).
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baselines(w, args.cpu_seconds)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -127,12 +133,25 @@ def main():
         return
 
     out = measure(w, args, primary=True)
+    out["cpu_baseline"] = cpu
+    out["run_conditions"] = run_conditions(torch)
     if not args.no_host_tier and w.name != HOST_TIER:
         h_args = argparse.Namespace(**vars(args))
         h_args.steps, h_args.warmup = 10, 2
         ht = measure(ALL[HOST_TIER], h_args, primary=False)
         out["host_tier"] = {k: ht[k] for k in ("config", "value", "unit", "ms_per_step", "steps",
                                                "kernels_us", "host_tier")}
+        # HBM held against context length with K/V in host memory: the same
+        # workload at 64K, 128K and 256K (budget held at ~3%)
+        points = []
+        for T in (65536, 131072):
+            wt = ALL[HOST_TIER].with_(name=f"qwen3-30b-a3b-host-tier-b4-t{T}", T=T,
+                                      k_chunk=T // 2048, k_group=T // 1024)
+            s_args = argparse.Namespace(**vars(h_args))
+            s_args.steps, s_args.warmup = 5, 1
+            points.append(measure(wt, s_args, primary=False))
+        points.append(ht)
+        out["host_tier"]["memory_slope"] = host_memory_slope(points)
     if not args.no_prefill and w.name != PREFILL:
         p_args = argparse.Namespace(**vars(args))
         p_args.steps, p_args.warmup = 5, 2
@@ -161,12 +180,12 @@ def main():
         w2 = ALL[SECONDARY]
         if w2.name != w.name:
             sec_args = argparse.Namespace(**vars(args))
-            sec_args.steps, sec_args.warmup = max(20, args.steps // 10), max(5, args.warmup // 4)
+            sec_args.steps, sec_args.warmup = max(50, args.steps // 4), max(5, args.warmup // 4)
             sec = measure(w2, sec_args, primary=False)
             out["secondary"] = {k: sec[k] for k in ("config", "value", "unit", "ms_per_step",
                                                     "steps", "hbm_gbs_step", "roofline",
                                                     "roofline_attend", "roofline_step",
-                                                    "roofline_build",
+                                                    "roofline_build", "warm_cache",
                                                     "kernels_us", "latency_us")}
     print(json.dumps(out))
 
@@ -366,22 +385,35 @@ def measure(w, args, primary: bool):
     assert float((O_step.float() - O.float()).abs().max()) <= 2e-2, "decode step != attend"
 
     use_graph = not args.no_graph
-    singles, chain = [], None
+
+    def capture(n, sets_used):
+        """One graph of exactly n steps, rotating over the first sets_used copies."""
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for k in range(n):
+                step(k % sets_used)
+        return gr
+
+    singles, graphs = [], {}
     if use_graph:
         for s in range(S):
             step(s)
         torch.cuda.synchronize()
-        for s in range(S):
+        for s in range(S):       # single steps, for the latency percentiles
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 step(s)
             singles.append(gr)
-        chain = torch.cuda.CUDAGraph()          # one rotation: S steps back to back
-        with torch.cuda.graph(chain):
-            for s in range(S):
-                step(s)
+        # The warm-up and the timed steps each replay one graph that holds
+        # exactly that many steps (cold: rotating over the S copies; warm: one
+        # copy, so the routed working set stays in the Infinity Cache), so that
+        # no per-replay launch cost is spread over a few steps.
+        for name, n, sets_used in (("warmup", args.warmup, S), ("cold", args.steps, S),
+                                   ("warm", args.steps, 1)):
+            if n > 0:
+                graphs[name] = capture(n, sets_used)
         torch.cuda.synchronize()
-    graphs_keep = (singles, chain)
+    graphs_keep = (singles, graphs)
 
     def run(k):
         if use_graph:
@@ -389,16 +421,15 @@ def measure(w, args, primary: bool):
         else:
             step(k % S)
 
-    def run_steps(n):
-        """Exactly n steps, starting at copy 0."""
-        k = 0
+    def run_steps(n, kind="cold"):
+        """Exactly n steps, starting at copy 0 (kind "warm": copy 0 only)."""
+        if n <= 0:
+            return
         if use_graph:
-            while n - k >= S:
-                chain.replay()
-                k += S
-        while k < n:
-            run(k)
-            k += 1
+            graphs[kind].replay()
+            return
+        for k in range(n):
+            step(0 if kind == "warm" else k % S)
 
     def busy_gpu():
         # Keep the GPU busy while the host enqueues, so that event pairs time
@@ -412,7 +443,7 @@ def measure(w, args, primary: bool):
                 a /= a.norm()
 
     # ---------------- timed region: exactly `steps` steps
-    run_steps(args.warmup)
+    run_steps(args.warmup, "warmup")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_steps(args.steps)
@@ -420,6 +451,18 @@ def measure(w, args, primary: bool):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = w.B * w.Nq / ((t1 - t0) / args.steps)
+
+    # ---------------- the same steps with warm caches (one K/V copy, so the
+    # routed working set stays in the Infinity Cache), beside the cold figure
+    run_steps(args.steps, "warm")
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    run_steps(args.steps, "warm")
+    torch.cuda.synchronize()
+    tw1 = time.perf_counter()
+    warm = {"ms_per_step": round((tw1 - tw0) * 1e3 / args.steps, 5),
+            "value": round(w.B * w.Nq / ((tw1 - tw0) / args.steps), 1), "unit": "tokens/s",
+            "steps": args.steps, "cache": "warm (one K/V copy reused every step)"}
 
     # ---------------- per-step latency percentiles (events between single-step replays)
     n_lat = max(50, min(args.steps, 400))
@@ -486,9 +529,13 @@ def measure(w, args, primary: bool):
     def roof(kernel, nbytes, us):
         traffic, _ = stored_traffic(kernel, w.name)
         achieved = nbytes / (us * 1e-6) / 1e9
+        # HBM bytes the counters saw per launch, over the same launch time
+        counter_gbs = round(traffic / (us * 1e-6) / 1e9, 1) if traffic else None
         return {"kernel": f"hga_{kernel}", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "alg_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
+                "traffic": traffic, "traffic_gbs": counter_gbs,
+                "traffic_over_alg": round(traffic / nbytes, 4) if traffic else None,
+                "alg_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
 
     # The attention kernel alone (it moves the routed K/V, almost all of a
     # step's bytes), and the whole step (one launch for small batches) against
@@ -498,15 +545,19 @@ def measure(w, args, primary: bool):
     roofline_attend["gathered_bytes_per_launch"] = gather_bytes
     roofline_attend["gathered_gbs"] = round(gather_bytes / (attend_us * 1e-6) / 1e9, 1)
     if tiles is not None:
-        # the tile kernel is a (masked) MFMA contraction: its executed flops
-        # against the dense bf16 peak; its bytes (each tile's union) beside
-        tf = tiles["executed_flops"] / (attend_us * 1e-6) / 1e12
+        # the tile kernel is a (masked) MFMA contraction: the method's flops
+        # (4 D per routed token) against the dense bf16 peak; the flops the
+        # masked tiles execute, and the bytes of each tile's union, beside
+        tf = tiles["alg_flops"] / (attend_us * 1e-6) / 1e12
+        tf_exec = tiles["executed_flops"] / (attend_us * 1e-6) / 1e12
         roofline_attend = {
-            "kernel": "hga_attend_tiles", "bound": "mfma", "achieved": round(tf, 1),
+            "kernel": "hga_attend_tiles", "bound": "mfma", "achieved": round(tf, 2),
             "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
-            "executed_flops_per_launch": tiles["executed_flops"],
+            "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 5), "traffic": None,
             "alg_flops_per_launch": tiles["alg_flops"],
+            "executed_flops_per_launch": tiles["executed_flops"],
+            "executed_tflops": round(tf_exec, 1),
+            "executed_frac": round(tf_exec / PEAK_MFMA_BF16_TFLOPS, 4),
             "bytes_per_launch": tiles["bytes"],
             "gbs": round(tiles["bytes"] / (attend_us * 1e-6) / 1e9, 1),
             "tiles": tiles["tiles"], "union_groups_per_tile": tiles["union_groups_per_tile"],
@@ -527,18 +578,16 @@ def measure(w, args, primary: bool):
         cand_flops = 2 * w.D * int((c >= 0).sum()) * gpc                  # the method's candidates
         executed = 2 * (2 * w.D * (w.n_chunks + w.n_groups) * rows_all)   # dense, hi and lo passes
         route_us = kern_us["route"]["avg"]
-        mfma = {"kernels": "route call: split + score_mfma + select",
-                "alg_flops": chunk_flops + cand_flops, "executed_flops": executed,
-                "route_us": round(route_us, 2),
+        alg = chunk_flops + cand_flops
+        mfma = {"kernels": "route call: split + route_prefill_fused (MFMA scoring, both selections)",
+                "alg_flops": alg, "chunk_gemm_flops": chunk_flops, "executed_flops": executed,
+                "route_us": round(route_us, 2), "peak_tflops": PEAK_MFMA_BF16_TFLOPS,
+                "achieved_tflops": round(alg / (route_us * 1e-6) / 1e12, 2),
+                "frac": round(alg / (route_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 5),
                 "achieved_tflops_executed": round(executed / (route_us * 1e-6) / 1e12, 1),
-                "peak_tflops": PEAK_MFMA_BF16_TFLOPS,
                 "frac_executed": round(executed / (route_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
-                "note": "time of the whole route call, so a lower bound for the MFMA kernel alone"}
-
-    # ---------------- CPU oracle baseline (host cores, bounded sample)
-    cpu = None
-    if primary and not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+                "counters": stored_counters_note("route_prefill", w.name),
+                "note": "time of the whole route call (split, scoring, selections)"}
 
     out = {
         "metric": METRIC,
@@ -572,7 +621,7 @@ def measure(w, args, primary: bool):
         "kernels_us": {k: round(v["avg"], 3) for k, v in kern_us.items()},
         "latency_us": {"p50": round(pct(lat, 0.5), 2), "p95": round(pct(lat, 0.95), 2),
                        "p99": round(pct(lat, 0.99), 2)},
-        "cpu_baseline": cpu,
+        "warm_cache": warm,
         "setup_s": {"generate": round(t_gen, 1)},
     }
     if quality is not None:
@@ -606,39 +655,151 @@ def quality_proxy(hga, torch, w, Q, K, V, gidx):
             "routed_fraction": round(w.k_group * w.group / w.T, 5)}
 
 
-def cpu_baseline(w, inp, seconds):
-    """The CPU oracle, as it stands, on the same decode step: refresh of the
-    newest chunk's summaries, routing and attention for every query head."""
-    import numpy as np
+# The oracle's workload for the forked CPU workers: set by the parent before
+# the pool starts, inherited by every worker.
+_CPU_JOB = None
+
+
+def _cpu_worker(seconds):
+    """Complete decode steps of the oracle, as it stands, in one thread, for
+    about `seconds`: the newest chunk's summaries recomputed, then routing and
+    attention for every query head. Returns (steps, elapsed seconds, step times)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
 
+    w, inp, cm0, gm0 = _CPU_JOB
+    cm, gm = cm0.copy(), gm0.copy()
+    c_first = (w.T - w.Nq) // w.chunk
+    lo = c_first * w.chunk
+
+    def one():
+        cm_l, gm_l = oracle.build_summaries(inp.K[:, :, lo:], w.chunk, w.group)
+        cm[:, :, c_first:] = cm_l
+        gm[:, :, lo // w.group:] = gm_l
+        _, gidx, _ = oracle.route(inp.Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
+        oracle.attend(inp.Q, inp.K, inp.V, gidx, w.group)
+
     with threadpool_limits(limits=1):
-        cm, gm = oracle.build_summaries(inp.K, w.chunk, w.group)   # setup, untimed
-        c_last = (w.T - 1) // w.chunk
-
-        def one():
-            lo = c_last * w.chunk
-            cm_l, gm_l = oracle.build_summaries(inp.K[:, :, lo:], w.chunk, w.group)
-            cm[:, :, c_last] = cm_l[:, :, 0]
-            gm[:, :, lo // w.group:] = gm_l
-            _, gidx, _ = oracle.route(inp.Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
-            oracle.attend(inp.Q, inp.K, inp.V, gidx, w.group)
-
         one()  # warm-up
         times = []
-        t_end = time.time() + seconds
-        while time.time() < t_end or len(times) < 3:
+        t_start = time.perf_counter()
+        t_end = t_start + seconds
+        while time.perf_counter() < t_end or len(times) < 3:
             t0 = time.perf_counter()
             one()
             times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": round(w.B * w.Nq / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} full decode steps of {w.name} (all {w.B * w.Hq * w.Nq} "
-                      f"query heads; newest-chunk summary refresh + routing + attention), "
-                      f"median {t * 1e3:.1f} ms, fp64 NumPy, 1 thread",
+        elapsed = time.perf_counter() - t_start
+    return len(times), elapsed, times
+
+
+def _cpu_run(w, seconds, workers):
+    """Tokens/s of the oracle on `workers` single-threaded processes, each
+    running whole decode steps of w concurrently (throughput = the sum of
+    their rates)."""
+    import multiprocessing
+
+    import oracle
+    from synth import generate
+
+    global _CPU_JOB
+    inp = generate(w, seed=0)
+    cm, gm = oracle.build_summaries(inp.K, w.chunk, w.group)   # setup, untimed
+    _CPU_JOB = (w, inp, cm, gm)
+    try:
+        if workers == 1:
+            res = [_cpu_worker(seconds)]
+        else:
+            with multiprocessing.get_context("fork").Pool(workers) as pool:
+                res = pool.map(_cpu_worker, [seconds] * workers)
+    finally:
+        _CPU_JOB = None
+    rate = sum(n / el for n, el, _ in res)            # decode steps per second, all workers
+    times = sorted(t for _, _, ts in res for t in ts)
+    med = times[len(times) // 2]
+    return {"value": round(w.B * w.Nq * rate, 2), "unit": "tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{sum(n for n, _, _ in res)} full decode steps of {w.name} "
+                      f"(all {w.B * w.Hq * w.Nq} query rows each; newest-chunk summary "
+                      f"refresh + routing + attention) over {workers} single-threaded "
+                      f"process(es) for ~{seconds:.0f} s, median step {med * 1e3:.1f} ms, "
+                      f"fp64 NumPy"}
+
+
+def cpu_baselines(w, seconds):
+    """The CPU oracle on the host's cores (at most 16, the CPU share of one
+    GPU), plus a one-thread pass at the batch-16 4K-context sweep point for
+    scaling context."""
+    from synth import SWEEP
+
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, affinity))
+    main = _cpu_run(w, seconds, workers)
+    one = _cpu_run(SWEEP[4096], max(3.0, seconds / 3), 1)
+    main["cpu_model"] = _cpu_model()
+    main["cpus_in_affinity"] = affinity
+    main["single_thread_b16_t4096"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    return main
+
+
+def run_conditions(torch):
+    """Device, software and clocks of this run."""
+    import subprocess
+
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    clocks = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode == 0:
+            d = json.loads(r.stdout)
+            card = next(iter(d.values()))
+            clocks = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:
+        pass
+    return {"device": props.name, "gfx": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1), "rocm": rocm,
+            "hip": torch.version.hip, "torch": torch.__version__, "clocks": clocks,
             "cpu_model": _cpu_model()}
+
+
+def host_memory_slope(points):
+    """HBM held by the host-tier step (K/V in host memory) at several context
+    lengths: bytes per context token, and the slope between the shortest and
+    the longest."""
+    rows = []
+    for r in points:
+        c, h = r["config"], r["host_tier"]
+        ctx = c["batch"] * c["seq_len"]
+        rows.append({"seq_len": c["seq_len"], "batch": c["batch"],
+                     "hbm_bytes_resident": h["hbm_bytes_resident"],
+                     "hbm_bytes_per_context_token": round(h["hbm_bytes_resident"] / ctx, 1),
+                     "kv_bytes_in_host_memory": h["kv_bytes_in_host_memory"],
+                     "fetched_bytes_per_token": h["fetched_bytes_per_token"],
+                     "value": r["value"], "unit": r["unit"]})
+    rows.sort(key=lambda x: x["seq_len"])
+    a, b = rows[0], rows[-1]
+    slope = (b["hbm_bytes_resident"] - a["hbm_bytes_resident"]) / (
+        b["batch"] * b["seq_len"] - a["batch"] * a["seq_len"])
+    return {"points": rows, "hbm_bytes_per_added_context_token": round(slope, 1),
+            "kv_bytes_per_context_token_in_host_memory":
+                round(b["kv_bytes_in_host_memory"] / (b["batch"] * b["seq_len"]), 1)}
+
+
+def stored_counters_note(kernel: str, workload: str):
+    """The derived line of a committed counter summary (profiles/), if any."""
+    path = os.path.join(ROOT, "profiles", f"hga_{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^counters_json: (\{.*\})\s*$", open(path).read(), flags=re.M)
+    return json.loads(m.group(1)) if m else None
 
 
 def _cpu_model():
