@@ -370,10 +370,10 @@ __device__ __forceinline__ void write_refreshed(const RouteArgs& a, int u, const
 }
 
 // Dynamic LDS of the step: the row's scores [n_c + n_g] | kept chunks [cap] |
-// chosen [max(k_c, k_g)] | the row's ids [k_g].
+// the row's group ids [k_g].
 inline size_t step_lds_bytes(const RouteArgs& a) {
   const int cap = kept_capacity(a);
-  return static_cast<size_t>(a.n_c + a.n_g + cap + max(a.k_c, a.k_g) + a.k_g) * 4;
+  return static_cast<size_t>(a.n_c + a.n_g + cap + a.k_g) * 4;
 }
 
 template <typename T, int D, int E>
@@ -408,8 +408,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   float* s_cs = s_dyn;               // chunk scores [n_c]
   float* s_gs = s_cs + ra.n_c;       // group scores [n_g]
   int* s_kept = reinterpret_cast<int*>(s_gs + ra.n_g);
-  int* s_pick = s_kept + cap;
-  int* s_ids = s_pick + max(ra.k_c, ra.k_g);
+  int* s_ids = s_kept + cap;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int L = p >= 0 ? p / ra.C : -1;
@@ -463,11 +462,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
       wave_lds_sync();
       return L + 1;
     }
-    const int gc = ra.k_c > 0 ? rowroute::wave_select<E>(
-                                    L - 1, ra.k_c, [&](int t) { return s_cs[1 + t]; }, s_pick)
-                              : 0;
-    wave_lds_sync();
-    for (int t = lane; t < gc; t += kWave) s_kept[1 + t] = 1 + s_pick[t];
+    // chunks 1..L-1 compete; the chosen ones land in s_kept[1..k_c] directly
+    if (ra.k_c > 0)
+      rowroute::wave_select_ids<E>(
+          L - 1, ra.k_c,
+          [&](int t, int& id) {
+            id = 1 + t;
+            return s_cs[1 + t];
+          },
+          s_kept + 1, nullptr);
     if (lane == 0) {
       s_kept[0] = 0;
       s_kept[ra.k_c + 1] = L;
@@ -522,18 +525,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
       const int k = pow2 ? t >> sh : t / gpc;
       return s_kept[k] * gpc + (t - k * gpc);
     };
+    int32_t* gout = split == 0 ? ra.group_idx + static_cast<size_t>(row) * ra.k_g : nullptr;
     if (p >= 0 && ok) {
       // level 2: the groups of the kept chunks that start at or before p; the
-      // invalid ones are the last kept chunk's (chunk L's) groups after p
+      // invalid ones are the last kept chunk's (chunk L's) groups after p. The
+      // chosen group ids go to s_ids (and split 0's to group_idx) directly.
       const int n_valid = (n_kept - 1) * gpc + min(gpc, p / ra.G - L * gpc + 1);
-      got = rowroute::wave_select<E>(n_valid, ra.k_g, [&](int t) { return s_gs[cand(t)]; },
-                                     s_pick);
-      wave_lds_sync();
+      got = rowroute::wave_select_ids<E>(
+          n_valid, ra.k_g,
+          [&](int t, int& id) {
+            id = cand(t);
+            return s_gs[id];
+          },
+          s_ids, gout);
     }
-    for (int t = lane; t < ra.k_g; t += kWave) {
-      const int g = t < got ? cand(s_pick[t]) : -1;
-      s_ids[t] = g;
-      if (split == 0) ra.group_idx[static_cast<size_t>(row) * ra.k_g + t] = g;
+    for (int t = got + lane; t < ra.k_g; t += kWave) {
+      s_ids[t] = -1;
+      if (gout) gout[t] = -1;
     }
     if (split == 0 && ra.chunk_idx) {
       for (int t = lane; t < ra.k_c + 2; t += kWave)
@@ -651,7 +659,7 @@ bool decode_step_one_launch(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int6
   // the score and partial words live in the workspace's zero-at-rest region
   if (step_words(rows, n_c + n_g, plan.n_splits, D).end > kStatusOffset) return false;
   const int64_t cap = std::min<int64_t>(k_c + 2, n_c);
-  const size_t lds = static_cast<size_t>(n_c + n_g + cap + std::max(k_c, k_g) + k_g) * 4;
+  const size_t lds = static_cast<size_t>(n_c + n_g + cap + k_g) * 4;
   return lds + step_static_lds(D) <= 160 * 1024;
 }
 

@@ -350,14 +350,38 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     }
     __syncthreads();
   }
+  // The splits' (m, l, o) in blocks of kMB splits, each block's LDS reads
+  // issued together: one LDS round trip per block rather than per split. The
+  // sums run in split order, as one split at a time would.
+  constexpr int kMB = 8;
   float Mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) Mx = fmaxf(Mx, s_part[s * (D + 2)]);
+  for (int s0 = 0; s0 < n_splits; s0 += kMB) {
+    float mv[kMB];
+#pragma unroll
+    for (int j = 0; j < kMB; ++j) mv[j] = s_part[min(s0 + j, kAttendMaxSplits - 1) * (D + 2)];
+#pragma unroll
+    for (int j = 0; j < kMB; ++j)
+      if (s0 + j < n_splits) Mx = fmaxf(Mx, mv[j]);
+  }
   float Lx = 0.f, ox = 0.f;
   if (Mx != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float f = exp2f(s_part[s * (D + 2)] - Mx);
-      Lx += s_part[s * (D + 2) + 1] * f;
-      if (d < D) ox += s_part[s * (D + 2) + 2 + d] * f;
+    for (int s0 = 0; s0 < n_splits; s0 += kMB) {
+      float mv[kMB], lv[kMB], ov[kMB];
+#pragma unroll
+      for (int j = 0; j < kMB; ++j) {
+        const float* ps = &s_part[min(s0 + j, kAttendMaxSplits - 1) * (D + 2)];
+        mv[j] = ps[0];
+        lv[j] = ps[1];
+        ov[j] = d < D ? ps[2 + d] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kMB; ++j) {
+        if (s0 + j < n_splits) {
+          const float f = exp2f(mv[j] - Mx);
+          Lx += lv[j] * f;
+          ox += ov[j] * f;
+        }
+      }
     }
   }
   finish(Mx, Lx, ox);

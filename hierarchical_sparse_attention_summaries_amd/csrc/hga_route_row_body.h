@@ -128,6 +128,43 @@ __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out
   return before;
 }
 
+// wave_select writing the chosen items' ids rather than their positions:
+// item(i, id) returns item i's score and sets its id; the ids of the chosen
+// items go, in ascending item order, to out[0..got) (LDS) and, when gout is
+// not null, to gout[0..got) too. Returns got.
+template <int E, typename Item>
+__device__ __forceinline__ int wave_select_ids(int n, int k, Item item, int* out, int32_t* gout) {
+  const int lane = lane_id();
+  uint32_t key[E];
+  int id[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * kWave + lane;
+    id[e] = -1;
+    key[e] = i < n ? order_key(item(i, id[e])) : 0u;
+  }
+  SelMask<E> chosen = 0;
+  if (n <= k) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) chosen |= static_cast<SelMask<E>>(key[e] != 0u) << e;
+  } else {
+    chosen = wave_top_k<E>(key, k);
+  }
+  int before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool c = (chosen >> e) & 1u;
+    const uint64_t m = ballot(c);
+    if (c) {
+      const int at = before + bits_below(m);
+      out[at] = id[e];
+      if (gout) gout[at] = id[e];
+    }
+    before += __popcll(m);
+  }
+  return before;
+}
+
 constexpr int kFreshChunks = 2;   // chunks a refresh of <= C newest keys can touch
 constexpr int kFreshMaxGpc = 16;  // groups per chunk the refresh keeps in LDS
 
