@@ -519,10 +519,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     // Candidate t of level 2 is group s_kept[t / gpc] * gpc + t % gpc (kept
     // chunks ascending, so the candidates ascend too).
     const int gpc = ra.gpc;
-    const bool pow2 = (gpc & (gpc - 1)) == 0;
-    const int sh = __builtin_ctz(static_cast<unsigned>(gpc));
+    // t / gpc as a multiply-high by ceil(2^32 / gpc): exact for t * gpc < 2^32
+    // (here t < 4096 items, gpc <= 512), and no branch
+    const uint64_t magic = (0x100000000ull + gpc - 1) / gpc;
     auto cand = [&](int t) {
-      const int k = pow2 ? t >> sh : t / gpc;
+      const int k = static_cast<int>((static_cast<uint64_t>(t) * magic) >> 32);
       return s_kept[k] * gpc + (t - k * gpc);
     };
     int32_t* gout = split == 0 ? ra.group_idx + static_cast<size_t>(row) * ra.k_g : nullptr;

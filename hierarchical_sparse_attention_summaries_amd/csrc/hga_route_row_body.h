@@ -101,14 +101,19 @@ constexpr int kGroupPassLean = 9;
 
 // Top-k of n keys held in LDS (`score(i)` gives item i's float score), by one
 // wave; writes the chosen item ids ascending to out[0..k) and returns how many.
+// Every lane reads an item whatever n (its index clamped to n - 1; item 0 must
+// be readable), so that the reads carry no branch and all issue together;
+// items past n get key 0.
 template <int E, typename ScoreOf>
 __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out) {
   const int lane = lane_id();
+  const int last = n > 0 ? n - 1 : 0;
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = e * kWave + lane;
-    key[e] = i < n ? order_key(score(i)) : 0u;
+    const float s = score(min(i, last));
+    key[e] = i < n ? order_key(s) : 0u;
   }
   SelMask<E> chosen = 0;
   if (n <= k) {
@@ -135,13 +140,14 @@ __device__ __forceinline__ int wave_select(int n, int k, ScoreOf score, int* out
 template <int E, typename Item>
 __device__ __forceinline__ int wave_select_ids(int n, int k, Item item, int* out, int32_t* gout) {
   const int lane = lane_id();
+  const int last = n > 0 ? n - 1 : 0;  // as wave_select: every lane reads an item
   uint32_t key[E];
   int id[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = e * kWave + lane;
-    id[e] = -1;
-    key[e] = i < n ? order_key(item(i, id[e])) : 0u;
+    const float s = item(min(i, last), id[e]);
+    key[e] = i < n ? order_key(s) : 0u;
   }
   SelMask<E> chosen = 0;
   if (n <= k) {
