@@ -12,11 +12,13 @@
 // rows as the A operand and the block's query rows as B, so that each lane
 // ends up with 8 scores of one row per group (two 16-token blocks); the online
 // softmax keeps (m, l) per row in the 4 lanes that hold it; O^T = V^T . P^T
-// with the staged V^T as A and the lane's own probabilities as B (the 32
-// tokens of a group in the lane order the scores came in), so each lane
-// accumulates 32 dims of its own row and the rescaling stays lane-local. One
-// operand read from LDS serves both row blocks. P enters the product as bf16
-// hi + lo parts, so the accumulation carries P to about 2^-17 relative.
+// with V^T as A and the lane's own probabilities as B (the 32 tokens of a
+// group in the lane order the scores came in), so each lane accumulates 32
+// dims of its own row and the rescaling stays lane-local. V is staged in LDS
+// row-major, as loaded, and its V^T operand comes from gfx950's transposed
+// LDS reads. One operand read from LDS serves both row blocks. P enters the
+// product rounded to bf16 (each weight within 2^-9 relative; l and the
+// accumulation stay fp32).
 #include <math.h>
 
 #include "hga_device.h"
@@ -37,18 +39,19 @@ constexpr int kTD = 128;                         // head dim
 constexpr int kSG = 1;                           // groups staged per step
 constexpr int kStageTok = kSG * kTG;
 constexpr int kKStride = kTD + 8;                // bf16 per staged K row (padded)
-constexpr int kVStride = kStageTok + 8;          // bf16 per staged V^T row (padded)
+// bf16 per staged V row (padded by 32 bytes: the 16 token rows one transposed
+// read touches then start 8 banks apart)
+constexpr int kVStride = kTD + 16;
 constexpr int kTileMaxGroups = 2048;             // groups of the context (mask rows)
-constexpr int kNK = kSG * kTG * 16 / kTThreads;  // K loads per thread per step
-constexpr int kNV = kSG * 16 * 16 / kTThreads;   // V token pairs per thread per step
-static_assert(kNK >= 1 && kNV >= 1, "every thread loads K and V");
+constexpr int kNK = kSG * kTG * 16 / kTThreads;  // K (and V) loads per thread per step
+static_assert(kNK >= 1, "every thread loads K and V");
 static_assert(kTR == 32 * kTW, "one 32-bit mask word per wave");
 
 struct TileLds {
   uint32_t mask[kTileMaxGroups][kTR / 32];       // rows of the tile that routed each group
   int list[kTileMaxGroups];                      // the union, ascending
   alignas(16) uint16_t k[kStageTok * kKStride];  // staged K rows
-  alignas(16) uint16_t vt[kTD * kVStride];       // staged V^T
+  alignas(16) uint16_t v[kStageTok * kVStride];  // staged V rows
   int wave_count[kTW];
 };
 
@@ -58,14 +61,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Two fp32 values as bf16 (round to nearest even, one conversion
-// instruction), and what those bf16 values leave over, also as bf16: x ~ hi + lo.
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float b0 = __uint_as_float(hi << 16), b1 = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - b0, x1 - b1}, bf16x2));
+// Two fp32 values as bf16 (round to nearest even, one conversion instruction).
+__device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
+
+// gfx950's transposed LDS read of 16-bit data: within each group of 16 lanes,
+// lane i receives, in slot j (0..3), element i % 4 of the four at the address
+// lane 4j + i / 4 gave (8-byte aligned).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Workgroup barrier ordering LDS only: unlike __syncthreads(), it does not
@@ -76,17 +85,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// V^T is staged with the token index of dim d XORed with vt_swizzle(d) (a
-// multiple of 4, so the 4-token blocks the operands read stay whole): the
-// transposing stores of a wave then spread over the LDS banks.
-__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) * 4; }
-
 // This thread's share of one step (zeros past the union's end, the context's
-// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K of step tokens
-// t / 16 + n * (threads / 16), and V of token pairs 2j, 2j + 1 of the step's
-// group pairs t / 16 + n * (threads / 16) (16 pairs per group).
+// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K and V of step
+// tokens t / 16 + n * (threads / 16).
 struct StepRegs {
-  uint4 k[kNK], v[2 * kNV];
+  uint4 k[kNK], v[kNK];
 };
 
 __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s, int n_u, int b,
@@ -114,19 +117,10 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
   for (int n = 0; n < kNK; ++n) {
     const int tg = t / 16 + n * (kTThreads / 16);  // step token
     const int gi = tg / kTG, x = tg % kTG;
-    r.k[n] = base[gi] >= 0 && x < n_tok[gi]
-                 ? ld16(K + base[gi] + static_cast<int64_t>(x) * kTD + col)
-                 : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int n = 0; n < kNV; ++n) {
-    const int pg = t / 16 + n * (kTThreads / 16);  // step token pair
-    const int gi = pg / 16, x = (pg % 16) * 2;
-#pragma unroll
-    for (int z = 0; z < 2; ++z)
-      r.v[2 * n + z] = base[gi] >= 0 && x + z < n_tok[gi]
-                           ? ld16(V + base[gi] + static_cast<int64_t>(x + z) * kTD + col)
-                           : make_uint4(0, 0, 0, 0);
+    const bool in = base[gi] >= 0 && x < n_tok[gi];
+    const int64_t at = base[gi] + static_cast<int64_t>(x) * kTD + col;
+    r.k[n] = in ? ld16(K + at) : make_uint4(0, 0, 0, 0);
+    r.v[n] = in ? ld16(V + at) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -134,23 +128,10 @@ __device__ __forceinline__ void stash_step(TileLds& s, const StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
 #pragma unroll
-  for (int n = 0; n < kNK; ++n)
-    *reinterpret_cast<uint4*>(&s.k[(t / 16 + n * (kTThreads / 16)) * kKStride + col]) = r.k[n];
-  // V^T: dims col .. col+7 of tokens x, x + 1 (one 32-bit word each)
-  uint32_t* vt = reinterpret_cast<uint32_t*>(s.vt);
-#pragma unroll
-  for (int n = 0; n < kNV; ++n) {
-    const int x = (t / 16 + n * (kTThreads / 16)) * 2;  // step token of the pair
-    const uint4 v0 = r.v[2 * n], v1 = r.v[2 * n + 1];
-    const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
-    const uint32_t a1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = col + 2 * e;
-      vt[(d * kVStride + (x ^ vt_swizzle(d))) / 2] = (a0[e] & 0xffffu) | (a1[e] << 16);
-      vt[((d + 1) * kVStride + (x ^ vt_swizzle(d + 1))) / 2] =
-          (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-    }
+  for (int n = 0; n < kNK; ++n) {
+    const int tg = t / 16 + n * (kTThreads / 16);
+    *reinterpret_cast<uint4*>(&s.k[tg * kKStride + col]) = r.k[n];
+    *reinterpret_cast<uint4*>(&s.v[tg * kVStride + col]) = r.v[n];
   }
 }
 
@@ -312,37 +293,38 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
           l[rb] += p[rb][tb][i];
         }
     }
-    // O^T += V^T . P^T, one group at a time, P as bf16 hi + lo; one V^T
-    // operand read serves both row blocks
+    // O^T += V^T . P^T, one group at a time, P as bf16; one V^T operand read
+    // serves both row blocks
 #pragma unroll
     for (int gi = 0; gi < kSG; ++gi) {
       if (bits[gi] == 0u) continue;  // uniform over the wave
-      bf16x8 ph[kRB], pl[kRB];
+      bf16x8 ph[kRB];
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
-        uint32_t hw[4], lw[4];
+        uint32_t hw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 2 * e;  // operand slots j, j + 1: block 2gi (j < 4) or 2gi + 1
-          split_pair(p[rb][2 * gi + j / 4][j % 4], p[rb][2 * gi + j / 4][j % 4 + 1], hw[e],
-                     lw[e]);
+          hw[e] = bf16_pair(p[rb][2 * gi + j / 4][j % 4], p[rb][2 * gi + j / 4][j % 4 + 1]);
         }
         ph[rb] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        pl[rb] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
 #pragma unroll
       for (int d = 0; d < kTD / 16; ++d) {
-        const int dim = d * 16 + lane % 16;
-        const uint16_t* vrow = &s.vt[dim * kVStride];
-        const int sw = vt_swizzle(dim);
-        const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + a4) ^ sw));
-        const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + ((gi * kTG + 16 + a4) ^ sw));
+        // This lane's V^T slice: dim d * 16 + lane % 16, tokens a4 .. a4 + 3 and
+        // 16 + a4 .. + 3 of group gi (the token order of its P^T slice). A
+        // transposed read hands lane i of each 16-lane group element i % 4 at
+        // the address of lane 4j + i / 4 (j = 0..3), so lane j16 of the group
+        // points at token a4 + j16 / 4, dims d * 16 + 4 * (j16 % 4) .. + 3.
+        const int j16 = lane % 16;
+        const uint16_t* src =
+            &s.v[(gi * kTG + a4 + j16 / 4) * kVStride + d * 16 + 4 * (j16 % 4)];
+        const uint2 x0 = lds_read_tr16(src);
+        const uint2 x1 = lds_read_tr16(src + 16 * kVStride);
         const bf16x8 va = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb)
           o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[rb], o[rb][d], 0, 0, 0);
-          o[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb], o[rb][d], 0, 0, 0);
-        }
       }
     }
   };
