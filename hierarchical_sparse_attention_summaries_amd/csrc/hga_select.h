@@ -42,11 +42,14 @@ __device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, i
     }
     if (a.k_c > 0) {
       // candidates: chunks 1 .. L-1, item t <-> chunk 1 + t
+      // every lane loads a valid score (index clamped; L - 1 > k_c >= 1
+      // chunks compete), so the loads carry no branch and are all in flight
       uint32_t key[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int t = e * kWave + lane;
-        key[e] = t < L - 1 ? order_key(load_shared(cs + 1 + t)) : 0u;
+        const float s = load_shared(cs + 1 + min(t, L - 2));
+        key[e] = t < L - 1 ? order_key(s) : 0u;
       }
       const SelMask<E> chosen = wave_top_k<E>(key, a.k_c);
       int before = 0;
@@ -72,14 +75,12 @@ __device__ __forceinline__ void select_row(const RouteArgs& a, int row, int p, i
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int t = e * kWave + lane;
-    bool valid = false;
-    int g = -1;
-    if (t < n_items) {
-      g = s_kept[t / a.gpc] * a.gpc + t % a.gpc;
-      valid = g < a.n_g && static_cast<int64_t>(g) * a.G <= p;
-    }
-    gid[e] = g;
-    key[e] = valid ? order_key(load_shared(gs + g)) : 0u;
+    const int tc = min(t, n_items - 1);  // every lane loads a valid group's score
+    const int g = s_kept[tc / a.gpc] * a.gpc + tc % a.gpc;
+    const bool valid = t < n_items && g < a.n_g && static_cast<int64_t>(g) * a.G <= p;
+    const float s = load_shared(gs + (g < a.n_g ? g : 0));
+    gid[e] = t < n_items ? g : -1;
+    key[e] = valid ? order_key(s) : 0u;
     n_valid += __popcll(ballot(valid));
   }
   SelMask<E> chosen = 0;

@@ -364,11 +364,14 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
       } else {
         n_kept = a.k_c + 2;
         if (a.k_c > 0) {
+          // every lane reads a valid score (index clamped; L - 1 > k_c >= 1
+          // chunks compete), so the reads carry no branch and issue together
           uint32_t key[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             const int u = e * kWave + lane;
-            key[e] = u < L - 1 ? order_key(cs[1 + u]) : 0u;
+            const float s = cs[1 + min(u, L - 2)];
+            key[e] = u < L - 1 ? order_key(s) : 0u;
           }
           const SelMask<E> chosen = wave_top_k<E>(key, a.k_c);
           int before = 0;
@@ -442,10 +445,12 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
     n_valid = static_cast<int>(wave_add(static_cast<uint32_t>(n_valid)));
     const float* gs = s_sc + t * lay.stride;
     uint32_t key[E];
+    const int u_last = n_valid > 0 ? n_valid - 1 : 0;  // reads clamped, as above
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int u = e * kWave + lane;
-      key[e] = u < n_valid ? order_key(gs[u]) : 0u;
+      const float s = gs[min(u, u_last)];
+      key[e] = u < n_valid ? order_key(s) : 0u;
     }
     SelMask<E> chosen = 0;
     if (n_valid <= a.k_g) {
