@@ -15,6 +15,8 @@ CPU-oracle baseline, per-kernel times, latency percentiles).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --only decode|attend|route|route_fresh|update|copy   # short runs for rocprofv3
+    HGA_LIB=hierarchical_sparse_attention_summaries_amd/libhga_phases.so python bench.py --phases
+        # per-phase clock stamps of the one-launch decode step (phase-stamp build)
 """
 from __future__ import annotations
 
@@ -59,6 +61,9 @@ def parse():
                     help="skip the 4096-query prefill step against a 64K cache (MFMA scoring)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the batch-16 context sweep below 64K (4096..32768 tokens)")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase stamps of the one-launch decode step (needs the phase-stamp "
+                         "build of the library, loaded through HGA_LIB)")
     return ap.parse_args()
 
 
@@ -120,6 +125,10 @@ def main():
         cpu = cpu_baselines(w, args.cpu_seconds)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.phases:
+        print(json.dumps(decode_phases(w, max(10, args.steps))))
+        return
 
     if args.only == "copy":
         # Plain copy of known size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE.
@@ -631,6 +640,84 @@ def measure(w, args, primary: bool):
     out["mfma"] = mfma
     del sets, graphs_keep
     return out
+
+
+PHASES = ["start", "scoring item done", "the row's older score words in LDS",
+          "chunk level selected (and the refreshed words in)", "group level selected, ids in LDS",
+          "wave 0's routed K/V folded in", "every wave's routed K/V folded in",
+          "split 0: the other splits' partials in", "split 0: hand-off words zeroed, splits merged", "end of the workgroup"]
+
+
+def decode_phases(w, steps):
+    """Clock stamps (100 MHz, chip-wide) at the end of each phase of the
+    one-launch decode step, from the phase-stamp build of the library: per
+    phase, the earliest, median and latest workgroup, in us after the step's
+    first workgroup started; medians over `steps` cold-cache steps."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_summaries_amd as hga
+    from synth import generate
+
+    L = hga.lib()
+    if not hasattr(L, "hga_debug_phase_stamps"):
+        sys.exit("bench.py --phases needs the phase-stamp build: run "
+                 "`python hierarchical_sparse_attention_summaries_amd/build.py --phase-stamps` "
+                 "and set HGA_LIB=hierarchical_sparse_attention_summaries_amd/libhga_phases.so")
+    L.hga_debug_phase_stamps.argtypes = [ctypes.c_void_p]
+    L.hga_debug_phase_stamps.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    inp = generate(w, seed=0)
+    Q = torch.from_numpy(inp.Q).to(dev, tdt)
+    K0 = torch.from_numpy(inp.K).to(dev, tdt)
+    V0 = torch.from_numpy(inp.V).to(dev, tdt)
+    cm0, gm0 = hga.build_summaries(K0, w.chunk, w.group)
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    if not hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group):
+        sys.exit(f"{w.name}: the decode step is not one launch here")
+    S = 15       # cold caches: rotate over copies, as the timed benchmark does
+    sets = [(K0, V0, cm0, gm0)] + [(K0.clone(), V0.clone(), cm0.clone(), gm0.clone())
+                                   for _ in range(S - 1)]
+    ws = torch.zeros(hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk,
+                                                     w.k_group), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        K, V, cm, gm = sets[s]
+        hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                           workspace=ws)
+
+    for k in range(30):
+        step(k % S)
+    torch.cuda.synchronize()
+    stamps = torch.zeros(4096 * 16, dtype=torch.int64, device=dev)
+    if L.hga_debug_phase_stamps(ctypes.c_void_p(stamps.data_ptr())) != 0:
+        sys.exit("could not set the phase-stamp buffer")
+    per = {k: [] for k in range(len(PHASES))}
+    grid = 0
+    for rep in range(steps):
+        stamps.zero_()
+        step(rep % S)
+        torch.cuda.synchronize()
+        a = stamps.view(-1, 16).cpu().numpy()
+        a = a[a[:, 0] > 0]
+        grid = len(a)
+        rel = (a - a[:, 0].min()) * 0.01      # 100 MHz ticks -> us
+        for k in range(len(PHASES)):
+            ok = a[:, k] > 0
+            if ok.any():
+                v = rel[ok, k]
+                per[k].append((float(v.min()), float(np.median(v)), float(v.max())))
+    L.hga_debug_phase_stamps(None)
+    out = {}
+    for k, name in enumerate(PHASES):
+        if per[k]:
+            out[f"{k} {name}"] = {q: round(statistics.median(x[j] for x in per[k]), 2)
+                                  for j, q in enumerate(("min", "median", "max"))}
+    return {"workload": w.name, "steps": steps, "workgroups": grid,
+            "unit": "us after the step's first workgroup started", "phases": out}
 
 
 def quality_proxy(hga, torch, w, Q, K, V, gidx):

@@ -24,7 +24,10 @@ __all__ = ["HGAError", "lib", "summary_counts", "build_summaries", "update_summa
            "decode_step_one_launch_cus", "workspace_check", "workspace_reset", "attend_staged", "decode_step_noalloc",
            "LIB_PATH", "WORKSPACE_ZERO_BYTES"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
+# The library is libhga.so beside this file; HGA_LIB may name another build of
+# it (the phase-stamp build, libhga_phases.so, for bench.py --phases).
+LIB_PATH = os.environ.get("HGA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libhga.so")
 
 F32, BF16 = 0, 1
 _STATUS = {0: "HGA_OK", -1: "HGA_ERR_NULL", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_DTYPE",

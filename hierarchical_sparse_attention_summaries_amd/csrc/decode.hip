@@ -31,6 +31,25 @@
 // reads every group summary (not only the candidates'), spread over every CU,
 // and saves the group level's dependent summary reads and the hand-over of
 // the ids between routing and attention.
+#include <hip/hip_runtime.h>
+
+// Phase stamps (a separate build with HGA_PHASE_STAMPS defined; off in the
+// library): thread 0 of every workgroup writes the chip-wide 100 MHz clock at
+// the end of each phase of the step to a buffer the host sets, slot
+// 16 * workgroup + phase.
+#ifdef HGA_PHASE_STAMPS
+__device__ unsigned long long* g_hga_phase_stamps;
+#define HGA_PHASE(k)                                                                    \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && g_hga_phase_stamps)                                         \
+      g_hga_phase_stamps[blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#else
+#define HGA_PHASE(k) \
+  do {               \
+  } while (0)
+#endif
+
 #include "hga_attend_body.h"
 #include "hga_route_row_body.h"
 
@@ -383,11 +402,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   __shared__ bool s_ok;
   const int bid = static_cast<int>(blockIdx.x);
   const int U = ra.B * ra.Hkv;
+  HGA_PHASE(0);
   // The workspace's status word, loaded first and read only after the scoring
   // item: non-zero if a wait of an earlier step on this workspace gave up.
   const int32_t status0 = load_shared_i32(aa.status);
   __shared__ FreshRows<D> s_fr;
   if (bid < U * st.items) score_item<T, D>(ra, st, bid % U, bid / U, s_fr);
+  HGA_PHASE(1);
   const int rows = ra.B * ra.Hq * ra.Nq;
   if (bid >= rows * st.n_splits) {
     if (bid < U) write_refreshed<D>(ra, bid, s_fr);
@@ -501,6 +522,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     if (!early) poll(cf, n1, gf, n2, threadIdx.x, kThreads);
   }
   __syncthreads();
+  HGA_PHASE(2);
   int n_kept = 0;
   if (early) {
     if (wave == 0) {
@@ -512,6 +534,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   } else if (wave == 0 && p >= 0 && !stale) {
     n_kept = level1();
   }
+  HGA_PHASE(3);
   const bool ok = s_ok;
   if (wave == 0) {
     int got = 0;
@@ -550,6 +573,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     }
   }
   __syncthreads();
+  HGA_PHASE(4);
   // Every split of the row has read the row's scores once all have counted
   // themselves in: the finishing workgroup then zeroes every word the scoring
   // wrote for the row (each one it saw arrive).
@@ -563,6 +587,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   attend_body<T, D, kWaves, true, decltype(zero_row), true>(aa, st.groups_per_wave, st.n_splits,
                                                            0, bid, s_ids, !ok, zero_row);
   if (bid < U) write_refreshed<D>(ra, bid, s_fr);
+  HGA_PHASE(9);
 }
 
 // Scoring items per unit: as many as the grid holds (at least two: the refresh
@@ -689,3 +714,12 @@ hipError_t launch_decode_step(const RouteArgs& ra, const AttendArgs& aa, const A
 }
 
 }  // namespace hga
+
+#ifdef HGA_PHASE_STAMPS
+// Sets the phase-stamp buffer of the one-launch decode step (16 x 8 bytes per
+// workgroup), or none with NULL. Phase-stamp builds only.
+extern "C" int hga_debug_phase_stamps(void* buffer) {
+  unsigned long long* p = static_cast<unsigned long long*>(buffer);
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_hga_phase_stamps), &p, sizeof(p)) == hipSuccess ? 0 : -7;
+}
+#endif

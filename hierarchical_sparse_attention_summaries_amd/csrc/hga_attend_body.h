@@ -211,6 +211,9 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
       }
     }
   }
+#ifdef HGA_PHASE
+  HGA_PHASE(5);  // wave 0's groups folded in
+#endif
   // Lanes of one column slot hold disjoint token rows: fold them.
   l = across_rows_sum<LPR>(l);
 #pragma unroll
@@ -225,6 +228,9 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     for (int k = 0; k < EPL; ++k) s_o[wave][col + k] = o[k];
   }
   __syncthreads();
+#ifdef HGA_PHASE
+  HGA_PHASE(6);  // every wave's groups folded in
+#endif
 
   float M = -INFINITY;
 #pragma unroll
@@ -316,6 +322,9 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
       if (a.status) store_shared_i32(a.status, kStatusTimedOut);
     }
     __syncthreads();
+#ifdef HGA_PHASE
+    HGA_PHASE(7);  // the other splits' partials in
+#endif
     if (!s_last) timed_out = true;
     // every other split has stored its partial, so is past the row's scores
     row_done();
@@ -384,6 +393,9 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
       }
     }
   }
+#ifdef HGA_PHASE
+  HGA_PHASE(8);  // merged
+#endif
   finish(Mx, Lx, ox);
   return true;
 }
