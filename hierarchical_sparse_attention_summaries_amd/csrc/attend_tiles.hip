@@ -85,6 +85,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// 16 bytes at byte offset `off` of a buffer; zeros where the buffer's range
+// ends before it (raw buffer loads return 0 out of range, so the load needs no
+// branch and the compiler can count it among the loads in flight).
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Buffer descriptor over `bytes` bytes from p (gfx9 raw buffer: stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
 // This thread's share of one step (zeros past the union's end, the context's
 // end, or a page out of range), dims (t % 16) * 8 .. +7 each: K and V of step
 // tokens t / 16 + n * (threads / 16).
@@ -96,31 +110,32 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
                                            int kv, int step, StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
-  const uint16_t* K = static_cast<const uint16_t*>(a.K);
-  const uint16_t* V = static_cast<const uint16_t*>(a.V);
-  // where each of the step's groups starts (a group lies within one page), and
-  // how many of its tokens the context holds
-  int64_t base[kSG];
-  int n_tok[kSG];
+  // each of the step's groups as a buffer over the tokens the context holds
+  // (a group lies within one page); an empty buffer past the union's end or
+  // for a page out of range
+  __amdgpu_buffer_rsrc_t rk[kSG], rv[kSG];
 #pragma unroll
   for (int gi = 0; gi < kSG; ++gi) {
     const int u = step * kSG + gi;
-    base[gi] = -1;
-    n_tok[gi] = 0;
+    int64_t base = -1;
+    int n_tok = 0;
     if (u < n_u) {
-      const int t0 = s.list[u] * kTG;
-      base[gi] = kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, t0);
-      n_tok[gi] = min(kTG, a.T - t0);
+      const int t0 = __builtin_amdgcn_readfirstlane(s.list[u]) * kTG;
+      base = kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, t0);
+      n_tok = min(kTG, a.T - t0);
     }
+    const int bytes = base >= 0 ? n_tok * kTD * 2 : 0;
+    const int64_t at = base >= 0 ? base : 0;
+    rk[gi] = buffer_of(static_cast<const uint16_t*>(a.K) + at, bytes);
+    rv[gi] = buffer_of(static_cast<const uint16_t*>(a.V) + at, bytes);
   }
 #pragma unroll
   for (int n = 0; n < kNK; ++n) {
     const int tg = t / 16 + n * (kTThreads / 16);  // step token
     const int gi = tg / kTG, x = tg % kTG;
-    const bool in = base[gi] >= 0 && x < n_tok[gi];
-    const int64_t at = base[gi] + static_cast<int64_t>(x) * kTD + col;
-    r.k[n] = in ? ld16(K + at) : make_uint4(0, 0, 0, 0);
-    r.v[n] = in ? ld16(V + at) : make_uint4(0, 0, 0, 0);
+    const int off = (x * kTD + col) * 2;
+    r.k[n] = buffer_ld16(rk[gi], off);
+    r.v[n] = buffer_ld16(rv[gi], off);
   }
 }
 
@@ -226,8 +241,9 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
 #pragma unroll
     for (int gi = 0; gi < kSG; ++gi) {
       const int u = step * kSG + gi;
-      g[gi] = u < n_u ? s.list[u] : -1;
-      bits[gi] = g[gi] >= 0 ? s.mask[g[gi]][wave] : 0u;
+      // uniform over the wave: read once, so the tests below branch on scalars
+      g[gi] = u < n_u ? __builtin_amdgcn_readfirstlane(s.list[u]) : -1;
+      bits[gi] = g[gi] >= 0 ? __builtin_amdgcn_readfirstlane(s.mask[g[gi]][wave]) : 0u;
       any |= bits[gi];
     }
     if (any == 0u) return;  // none of the wave's rows takes these groups
