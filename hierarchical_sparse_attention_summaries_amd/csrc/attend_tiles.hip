@@ -50,8 +50,8 @@ static_assert(kTR == 32 * kTW, "one 32-bit mask word per wave");
 struct TileLds {
   uint32_t mask[kTileMaxGroups][kTR / 32];       // rows of the tile that routed each group
   int list[kTileMaxGroups];                      // the union, ascending
-  alignas(16) uint16_t k[kStageTok * kKStride];  // staged K rows
-  alignas(16) uint16_t v[kStageTok * kVStride];  // staged V rows
+  alignas(16) uint16_t k[2][kStageTok * kKStride];  // staged K rows, two steps
+  alignas(16) uint16_t v[2][kStageTok * kVStride];  // staged V rows, two steps
   int wave_count[kTW];
 };
 
@@ -139,14 +139,14 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
   }
 }
 
-__device__ __forceinline__ void stash_step(TileLds& s, const StepRegs& r) {
+__device__ __forceinline__ void stash_step(TileLds& s, int buf, const StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
 #pragma unroll
   for (int n = 0; n < kNK; ++n) {
     const int tg = t / 16 + n * (kTThreads / 16);
-    *reinterpret_cast<uint4*>(&s.k[tg * kKStride + col]) = r.k[n];
-    *reinterpret_cast<uint4*>(&s.v[tg * kVStride + col]) = r.v[n];
+    *reinterpret_cast<uint4*>(&s.k[buf][tg * kKStride + col]) = r.k[n];
+    *reinterpret_cast<uint4*>(&s.v[buf][tg * kVStride + col]) = r.v[n];
   }
 }
 
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   }
 
   // One step: kSG groups of the union, staged in LDS.
-  auto compute = [&](int step) {
+  auto compute = [&](int step, int buf) {
     int g[kSG];
     uint32_t bits[kSG];  // the wave's 32 rows that routed each group
     uint32_t any = 0u;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
 #pragma unroll
       for (int ks = 0; ks < kTD / 32; ++ks) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &s.k[(tb * 16 + lane % 16) * kKStride + ks * 32 + a8]));
+            &s.k[buf][(tb * 16 + lane % 16) * kKStride + ks * 32 + a8]));
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
           sacc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(qB[rb][ks]),
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
         // points at token a4 + j16 / 4, dims d * 16 + 4 * (j16 % 4) .. + 3.
         const int j16 = lane % 16;
         const uint16_t* src =
-            &s.v[(gi * kTG + a4 + j16 / 4) * kVStride + d * 16 + 4 * (j16 % 4)];
+            &s.v[buf][(gi * kTG + a4 + j16 / 4) * kVStride + d * 16 + 4 * (j16 % 4)];
         const uint2 x0 = lds_read_tr16(src);
         const uint2 x1 = lds_read_tr16(src + 16 * kVStride);
         const bf16x8 va = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
@@ -345,24 +345,27 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     }
   };
 
-  // 4. The union in steps of kSG groups; each step's loads go out two steps
-  // ahead of its use (two workgroups per CU: 64 KiB in flight).
+  // 4. The union in steps of kSG groups, through two LDS buffers: step st is
+  // computed from buffer st % 2 while step st + 1 is stashed into the other,
+  // so one barrier per step both publishes st + 1 and frees buffer st % 2;
+  // a step's loads go out two computed steps before it is stashed.
   const int n_st = (n_u + kSG - 1) / kSG;
   StepRegs r0, r1;
   fetch_step(a, s, n_u, b, kv, 0, r0);
   fetch_step(a, s, n_u, b, kv, 1, r1);
+  stash_step(s, 0, r0);
+  lds_barrier();
+  fetch_step(a, s, n_u, b, kv, 2, r0);
   for (int st = 0; st < n_st; st += 2) {
-    stash_step(s, r0);
-    lds_barrier();
-    fetch_step(a, s, n_u, b, kv, st + 2, r0);
-    compute(st);
+    compute(st, 0);
+    stash_step(s, 1, r1);
     lds_barrier();
     if (st + 1 >= n_st) break;
-    stash_step(s, r1);
-    lds_barrier();
     fetch_step(a, s, n_u, b, kv, st + 3, r1);
-    compute(st + 1);
+    compute(st + 1, 1);
+    stash_step(s, 0, r0);
     lds_barrier();
+    fetch_step(a, s, n_u, b, kv, st + 4, r0);
   }
 
   // 5. Each row's total over its 4 lanes; each lane writes 32 dims of its rows.
