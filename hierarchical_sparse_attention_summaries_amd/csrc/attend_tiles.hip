@@ -85,20 +85,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// 16 bytes at byte offset `off` of a buffer; zeros where the buffer's range
-// ends before it (raw buffer loads return 0 out of range, so the load needs no
-// branch and the compiler can count it among the loads in flight).
-__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Buffer descriptor over `bytes` bytes from p (gfx9 raw buffer: stride 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
-
 // This thread's share of one step (zeros past the union's end, the context's
 // end, or a page out of range), dims (t % 16) * 8 .. +7 each: K and V of step
 // tokens t / 16 + n * (threads / 16).

@@ -131,19 +131,18 @@ __device__ __forceinline__ bool attend_body(const AttendArgs& a, int groups_per_
     t0 = s0;
     t1 = s1;
   };
-  // Issue the loads of up to kAttendTile tokens from `base` (rows >= t1 read as 0).
+  // Issue the loads of up to kAttendTile tokens from `base` (rows >= t1 read as
+  // 0): buffers over rows [base, t1) of the group, so no load sits in a branch.
   auto load = [&](int base, int t1, int64_t off, int t0, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+    const int bytes = max(0, t1 - base) * D * static_cast<int>(sizeof(TKV));
+    const int64_t at = off + static_cast<int64_t>(base - t0) * D;  // row `base` of the group
+    const __amdgpu_buffer_rsrc_t rk = buffer_of(Kbase + at, bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_of(Vbase + at, bytes);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int t = base + u * RPL + sub;
-      if (t < t1) {
-        const int64_t at = off + static_cast<int64_t>(t - t0) * D + col;  // row t of the group
-        kr[u] = ld16(Kbase + at);
-        vr[u] = ld16(Vbase + at);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int off_b = ((u * RPL + sub) * D + col) * static_cast<int>(sizeof(TKV));
+      kr[u] = buffer_ld16(rk, off_b);
+      vr[u] = buffer_ld16(rv, off_b);
     }
   };
   // Fold one loaded tile into (m, l, o). Token `base` must be valid.

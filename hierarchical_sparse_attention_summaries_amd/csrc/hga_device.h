@@ -20,6 +20,20 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// A raw buffer (stride 0) over `bytes` bytes from p, which must be the same in
+// every lane, and 16-byte loads from it at byte offset `off` that read zeros
+// past its end. Such a load needs no branch around it, so the compiler can
+// keep counting it among the loads in flight (a branch makes it wait for all).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Widen one 16-byte chunk to fp32.
 __device__ __forceinline__ void widen(const uint4& u, float (&x)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
