@@ -289,16 +289,16 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
   }
   const uint16_t* hi_base = a.split + static_cast<size_t>(bkv) * 2 * N * D;
   const uint16_t* lo_base = hi_base + static_cast<size_t>(N) * D;
+  // Split rows of column col (zeros at or past `limit`), through buffers over
+  // the rows below it, so that no load sits in a branch.
   auto load_b = [&](int col, int limit, uint4 (&h)[KS], uint4 (&l)[KS]) {
+    const __amdgpu_buffer_rsrc_t rh = buffer_of(hi_base, limit * D * 2);
+    const __amdgpu_buffer_rsrc_t rl = buffer_of(lo_base, limit * D * 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (col < limit) {
-        h[ks] = ld16(hi_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
-        l[ks] = ld16(lo_base + static_cast<size_t>(col) * D + ks * 32 + lk * 8);
-      } else {
-        h[ks] = make_uint4(0, 0, 0, 0);
-        l[ks] = make_uint4(0, 0, 0, 0);
-      }
+      const int off = (col * D + ks * 32 + lk * 8) * 2;
+      h[ks] = buffer_ld16(rh, off);
+      l[ks] = buffer_ld16(rl, off);
     }
   };
   auto mfma = [&](const uint4 (&h)[KS], const uint4 (&l)[KS], f32x4 (&acc)[RB]) {
@@ -316,20 +316,25 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
     }
   };
   // 16-column blocks of summary rows [col0, limit): this wave takes blocks
-  // wave, wave + W, ...; the next block's operands load while one runs.
+  // wave, wave + W, ...; the next block's operands load while one runs (a
+  // block past the end loads zeros without touching memory, so every load is
+  // issued unconditionally and the wait before a block's products leaves the
+  // next block's loads in flight).
   // consume(first column, acc): lane holds rows rb*16 + lk*4 + i, column + lr.
   auto sweep = [&](int col0, int limit, auto&& consume) {
     const int nblk = (limit - col0 + 15) / 16;
     uint4 hA[KS], lA[KS], hB[KS], lB[KS];
     f32x4 acc[RB];
     int cb = wave;
-    if (cb < nblk) load_b(col0 + cb * 16 + lr, limit, hA, lA);
+    load_b(col0 + cb * 16 + lr, limit, hA, lA);
     for (; cb < nblk; cb += 2 * W) {
-      if (cb + W < nblk) load_b(col0 + (cb + W) * 16 + lr, limit, hB, lB);
+      load_b(col0 + (cb + W) * 16 + lr, limit, hB, lB);
+      __builtin_amdgcn_sched_barrier(0);
       mfma(hA, lA, acc);
       consume(col0 + cb * 16, acc);
       if (cb + W >= nblk) break;
-      if (cb + 2 * W < nblk) load_b(col0 + (cb + 2 * W) * 16 + lr, limit, hA, lA);
+      load_b(col0 + (cb + 2 * W) * 16 + lr, limit, hA, lA);
+      __builtin_amdgcn_sched_barrier(0);
       mfma(hB, lB, acc);
       consume(col0 + (cb + W) * 16, acc);
     }
