@@ -418,18 +418,22 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
     }
   sweep(a.n_c, N, [&](int c0, const f32x4 (&acc)[RB]) {
     const int g = c0 + lr - a.n_c;
-    if (g >= a.n_g) return;
-    const int c = g >> gpc_shift;
+    // the chunk's rank in each of the lane's rows, all read at once (the
+    // chunk clamped into the table; g <= g_last implies g < n_g)
+    const int c = min(g, a.n_g - 1) >> gpc_shift;
     const int slot = g & gmask;
+    int rk[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rk[rb][i] = s_rank[(rb * 16 + lk * 4 + i) * rank_stride + c];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = rb * 16 + lk * 4 + i;
-        if (g <= g_last[rb][i]) {
-          const int rk = s_rank[t * rank_stride + c];
-          if (rk != 0xFF) s_sc[t * lay.stride + (rk << gpc_shift) + slot] = acc[rb][i] * a.scale;
-        }
+        if (g <= g_last[rb][i] && rk[rb][i] != 0xFF)
+          s_sc[t * lay.stride + (rk[rb][i] << gpc_shift) + slot] = acc[rb][i] * a.scale;
       }
   });
   __syncthreads();
