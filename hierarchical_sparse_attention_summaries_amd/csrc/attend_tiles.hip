@@ -85,9 +85,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// This thread's share of one step (zeros past the union's end, the context's
-// end, or a page out of range), dims (t % 16) * 8 .. +7 each: K and V of step
-// tokens t / 16 + n * (threads / 16).
+// This thread's share of one step (zeros past the union's end or the
+// context's end), dims (t % 16) * 8 .. +7 each: K and V of step tokens
+// t / 16 + n * (threads / 16).
 struct StepRegs {
   uint4 k[kNK], v[kNK];
 };
@@ -166,7 +166,8 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   __syncthreads();
 
   // 2. The union of the tile's groups, ascending: slot j covers groups
-  // [j * threads, +threads), one per thread.
+  // [j * threads, +threads), one per thread. A group on a page outside the
+  // pool is left out, as if no row had routed it (its keys are not there).
   int n_u = 0;
   for (int base = 0; base < n_g; base += kTThreads) {
     const int g = base + tid;
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
     if (g < n_g) {
 #pragma unroll
       for (int w = 0; w < kTR / 32; ++w) present = present || s.mask[g][w] != 0u;
+      if (present && a.kv.paged) present = kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, g * kTG) >= 0;
     }
     const uint64_t m = ballot(present);
     if (lane == 0) s.wave_count[wave] = __popcll(m);

@@ -318,7 +318,7 @@ def _pages(w, inp, seq_lens, page_tokens, seed=5):
     need = [-(-int(t) // page_tokens) for t in seq_lens]
     n_pages = sum(need) + 3
     order = rng.permutation(n_pages)
-    max_pages = w.T // page_tokens
+    max_pages = -(-w.T // page_tokens)
     table = np.full((w.B, max_pages), -1, dtype=np.int32)
     kp = np.zeros((n_pages, w.Hkv, page_tokens, w.D), dtype=np.float32)
     vp = np.zeros_like(kp)
@@ -327,8 +327,10 @@ def _pages(w, inp, seq_lens, page_tokens, seed=5):
         for j in range(need[b]):
             pid = int(order[k]); k += 1
             table[b, j] = pid
-            kp[pid] = inp.K[b, :, j * page_tokens:(j + 1) * page_tokens]
-            vp[pid] = inp.V[b, :, j * page_tokens:(j + 1) * page_tokens]
+            seg = slice(j * page_tokens, (j + 1) * page_tokens)   # the last may be partial
+            n = inp.K[b, :, seg].shape[1]
+            kp[pid, :, :n] = inp.K[b, :, seg]
+            vp[pid, :, :n] = inp.V[b, :, seg]
     return (to_dev(kp, w.dtype), to_dev(vp, w.dtype),
             torch.from_numpy(table).cuda(), n_pages)
 
@@ -342,6 +344,55 @@ def test_ragged_dense_cache(Nq):
     out = _run_ragged(w, inp, seq_lens, layout, to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype))
     from tests.gpu_runner import check_ragged
     check_ragged(w, inp, seq_lens, out)
+
+
+def _ids_with_strays(w, rng):
+    """Per row: up to 9 distinct groups at or before the row's position (its
+    own group, partly after it, always among them), then ids no group has:
+    n_g, n_g + 7 and -5."""
+    n_g = -(-w.T // w.group)
+    gidx = np.full((w.B, w.Hq, w.Nq, w.k_group), -1, dtype=np.int32)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for i in range(w.Nq):
+                own = (w.T - w.Nq + i) // w.group
+                pick = rng.choice(own, size=min(8, own), replace=False) if own > 0 else []
+                ids = [own, *[int(x) for x in pick], n_g, n_g + 7, -5]
+                gidx[b, h, i, :len(ids)] = ids[:w.k_group]
+    return gidx
+
+
+@pytest.mark.parametrize("nq", [1, 160])
+def test_attend_ignores_ids_and_pages_out_of_range(nq):
+    """Group ids outside [0, n_g), and routed groups whose page id lies outside
+    the pool, contribute nothing: the outputs equal the oracle's attention over
+    the other groups, on a dense and on a paged cache. Nq = 1 runs the per-row
+    gather, Nq = 160 the tile attention (bf16, D 128, G 32); both read a group's
+    rows through a range that ends where its valid rows end."""
+    log(f"case out-of-range ids and pages Nq={nq}")
+    w = Workload(f"stray-ids-nq{nq}", 1, 4, 2, 128, 2000, nq, 128, 32, 4, 12, 1e4, "bf16", 0)
+    inp = generate(w)
+    gidx_np = _ids_with_strays(w, np.random.default_rng(11))
+    Q = to_dev(inp.Q, w.dtype)
+    gidx = torch.from_numpy(gidx_np).cuda()
+    O, lse = hga.attend(Q, to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype), gidx, w.group)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attend(inp.Q, inp.K, inp.V, gidx_np, w.group)
+    parity.check_outputs(np_of(O), lse.cpu().numpy(), O_ref, lse_ref, w.dtype)
+
+    # paged: pages 3 and 10 point past the pool, page 20 before it
+    page_tokens = 64
+    kp, vp, table, n_pages = _pages(w, inp, [w.T], page_tokens)
+    bad = {3: n_pages + 3, 10: n_pages, 20: -2}
+    for j, pid in bad.items():
+        table[0, j] = pid
+    layout = hga.Layout(block_table=table, page_tokens=page_tokens, n_pages=n_pages)
+    O2, lse2 = hga.attend_ex(Q, kp, vp, gidx, w.group, layout=layout, seq_len=w.T)
+    torch.cuda.synchronize()
+    per = page_tokens // w.group
+    gone = np.isin(gidx_np // per, list(bad)) & (gidx_np >= 0)
+    O2_ref, lse2_ref = oracle.attend(inp.Q, inp.K, inp.V, np.where(gone, -1, gidx_np), w.group)
+    parity.check_outputs(np_of(O2), lse2.cpu().numpy(), O2_ref, lse2_ref, w.dtype)
 
 
 def test_paged_cache_matches_ragged_dense():
