@@ -373,12 +373,25 @@ def test_attend_ignores_ids_and_pages_out_of_range(nq):
     w = Workload(f"stray-ids-nq{nq}", 1, 4, 2, 128, 2000, nq, 128, 32, 4, 12, 1e4, "bf16", 0)
     inp = generate(w)
     gidx_np = _ids_with_strays(w, np.random.default_rng(11))
+    # a few rows of head 1 list stray ids only: no token, so O = 0, lse = -inf
+    empty = [i for i in (0, 77, nq - 1) if i < nq]
+    ids_empty = gidx_np.copy()
+    ids_empty[0, 1, empty] = -1
+    ids_empty[0, 1, empty, :3] = [-(2 ** 31), 10 ** 6, -3]
     Q = to_dev(inp.Q, w.dtype)
-    gidx = torch.from_numpy(gidx_np).cuda()
+
+    def check(O, lse, ids_ref):
+        O, lse = np_of(O), lse.cpu().numpy()
+        assert (O[0, 1, empty] == 0).all() and np.isneginf(lse[0, 1, empty]).all()
+        O_ref, lse_ref = oracle.attend(inp.Q, inp.K, inp.V, ids_ref, w.group)
+        O_ref[0, 1, empty] = 0
+        lse[0, 1, empty] = lse_ref[0, 1, empty] = 0
+        parity.check_outputs(O, lse, O_ref, lse_ref, w.dtype)
+
+    gidx = torch.from_numpy(ids_empty).cuda()
     O, lse = hga.attend(Q, to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype), gidx, w.group)
     torch.cuda.synchronize()
-    O_ref, lse_ref = oracle.attend(inp.Q, inp.K, inp.V, gidx_np, w.group)
-    parity.check_outputs(np_of(O), lse.cpu().numpy(), O_ref, lse_ref, w.dtype)
+    check(O, lse, gidx_np)   # the oracle sees the empty rows' original ids (it needs a token)
 
     # paged: pages 3 and 10 point past the pool, page 20 before it
     page_tokens = 64
@@ -391,8 +404,7 @@ def test_attend_ignores_ids_and_pages_out_of_range(nq):
     torch.cuda.synchronize()
     per = page_tokens // w.group
     gone = np.isin(gidx_np // per, list(bad)) & (gidx_np >= 0)
-    O2_ref, lse2_ref = oracle.attend(inp.Q, inp.K, inp.V, np.where(gone, -1, gidx_np), w.group)
-    parity.check_outputs(np_of(O2), lse2.cpu().numpy(), O2_ref, lse2_ref, w.dtype)
+    check(O2, lse2, np.where(gone, -1, gidx_np))
 
 
 def test_paged_cache_matches_ragged_dense():
