@@ -237,6 +237,31 @@ def test_explicit_scale():
     check_workload(w, inp, out, scale=0.05)
 
 
+@pytest.mark.parametrize("path", ["decode-step", "prefill-tiles", "many-row-route"])
+def test_explicit_scale_every_path(path):
+    """A caller's scale reaches every path that applies it itself: the
+    one-launch decode step, the prefill MFMA route with the tile attention, and
+    the many-row route; each against the oracle at that scale."""
+    s = 0.05
+    log(f"case explicit-scale {path}")
+    if path == "decode-step":
+        w = DECODE_64K.with_(T=4096, k_chunk=4, k_group=8)
+        shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+        assert hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+        inp = generate(w)
+        Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+        cm, gm = hga.build_summaries(K, w.chunk, w.group)
+        O, lse, c_d, g_d = hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk,
+                                              w.k_group, scale=s)
+        torch.cuda.synchronize()
+        out = dict(cm=cm, gm=gm, cidx=c_d, gidx=g_d, O=O, lse=lse)
+    else:
+        w = PREFILL_TILES[0] if path == "prefill-tiles" else FUSED_ROUTE[0]
+        inp = generate(w)
+        out = run_hip(w, inp, scale=s)
+    check_workload(w, inp, out, scale=s)
+
+
 def test_kv_in_pinned_host_memory():
     log("case pinned-host-kv")
     w = DECODE_64K.with_(T=8192, k_chunk=4, k_group=8, B=2)
