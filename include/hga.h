@@ -198,8 +198,10 @@ typedef struct hga_kv_layout {
   int32_t kind;                /* hga_kv_kind */
   int32_t page_tokens;         /* paged: tokens per page, a multiple of `group` */
   int32_t max_pages;           /* paged: columns of block_table, >= ceil(T / page_tokens) */
-  int32_t n_pages;             /* paged: pages in the pool; ids outside [0, n_pages) are
-                                  skipped (their tokens count as absent) */
+  int32_t n_pages;             /* paged: pages in the pool; a page id outside [0, n_pages)
+                                  holds no keys: attention skips the groups on it (their
+                                  tokens count as absent), and the summaries take its
+                                  tokens as zero keys (a group mean of 0) */
   const int32_t* block_table;  /* paged: [B, max_pages] int32 page ids, device memory;
                                   token t of sequence b is row t % page_tokens of page
                                   block_table[b][t / page_tokens] */
