@@ -22,8 +22,11 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 
 // A raw buffer (stride 0) over `bytes` bytes from p, which must be the same in
 // every lane, and 16-byte loads from it at byte offset `off` that read zeros
-// past its end. Such a load needs no branch around it, so the compiler can
-// keep counting it among the loads in flight (a branch makes it wait for all).
+// past its end (the callers' offsets and sizes are multiples of 16, so a load
+// lies wholly inside or wholly outside). Such a load needs no branch around
+// it, so the compiler can keep counting it among the loads in flight (a branch
+// makes it wait for all). 0x00020000 is the descriptor's fourth word with a
+// 32-bit data format, as gfx9-family raw buffer accesses use.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
