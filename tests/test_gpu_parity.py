@@ -391,9 +391,10 @@ def _ids_with_strays(w, rng):
 def test_attend_ignores_ids_and_pages_out_of_range(nq):
     """Group ids outside [0, n_g), and routed groups whose page id lies outside
     the pool, contribute nothing: the outputs equal the oracle's attention over
-    the other groups, on a dense and on a paged cache. Nq = 1 runs the per-row
-    gather, Nq = 160 the tile attention (bf16, D 128, G 32); both read a group's
-    rows through a range that ends where its valid rows end."""
+    the other groups, on a dense and on a paged cache, and staged attention
+    equals the direct one. Nq = 1 runs the per-row gather, Nq = 160 the tile
+    attention (bf16, D 128, G 32); both read a group's rows through a range
+    that ends where its valid rows end."""
     log(f"case out-of-range ids and pages Nq={nq}")
     w = Workload(f"stray-ids-nq{nq}", 1, 4, 2, 128, 2000, nq, 128, 32, 4, 12, 1e4, "bf16", 0)
     inp = generate(w)
@@ -414,9 +415,14 @@ def test_attend_ignores_ids_and_pages_out_of_range(nq):
         parity.check_outputs(O, lse, O_ref, lse_ref, w.dtype)
 
     gidx = torch.from_numpy(ids_empty).cuda()
-    O, lse = hga.attend(Q, to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype), gidx, w.group)
+    K, V = to_dev(inp.K, w.dtype), to_dev(inp.V, w.dtype)
+    O, lse = hga.attend(Q, K, V, gidx, w.group)
     torch.cuda.synchronize()
     check(O, lse, gidx_np)   # the oracle sees the empty rows' original ids (it needs a token)
+    # staged attention (routed groups copied into a pool first) ignores them alike
+    O3, lse3 = hga.attend_staged(Q, K, V, gidx, w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(O3, O) and torch.equal(lse3, lse)
 
     # paged: pages 3 and 10 point past the pool, page 20 before it
     page_tokens = 64
