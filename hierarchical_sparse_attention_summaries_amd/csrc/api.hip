@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
+#include <initializer_list>
 
 #include "hga.h"
 #include "hga_internal.h"
@@ -67,6 +68,15 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the product of non-negative factors is below `limit`, without
+// overflowing on the way (any factor may be as large as the caller passes).
+bool product_below(std::initializer_list<int64_t> factors, int64_t limit) {
+  int64_t p = 1;
+  for (const int64_t f : factors)
+    if (f < 0 || __builtin_mul_overflow(p, f, &p)) return false;
+  return p < limit;
+}
+
 int dtype_ok(int32_t dtype) { return dtype == HGA_F32 || dtype == HGA_BF16; }
 
 int check_chunking(int64_t T, int32_t chunk, int32_t group) {
@@ -83,9 +93,9 @@ int check_shape(const hga_shape* s) {
   if (s->q_heads % s->kv_heads != 0) return HGA_ERR_SHAPE;
   if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_SHAPE;
   if (s->n_queries > s->seq_len) return HGA_ERR_SHAPE;
-  const int64_t rows = s->batch * s->q_heads * s->n_queries;
-  if (s->batch >= kMaxDim || s->q_heads >= kMaxDim || s->seq_len >= kMaxDim || rows >= kMaxDim ||
-      s->batch * s->kv_heads * s->seq_len >= (int64_t(1) << 40))
+  if (s->batch >= kMaxDim || s->q_heads >= kMaxDim || s->seq_len >= kMaxDim ||
+      !product_below({s->batch, s->q_heads, s->n_queries}, kMaxDim) ||
+      !product_below({s->batch, s->kv_heads, s->seq_len}, int64_t(1) << 40))
     return HGA_ERR_SHAPE;
   return HGA_OK;
 }
@@ -102,7 +112,7 @@ int check_route_params(const hga_shape* s, int32_t chunk, int32_t group, int32_t
   if (n_c - 2 > hga::kMaxSelectItems || kept * gpc > hga::kMaxSelectItems ||
       kept > hga::kMaxKeptChunks)
     return HGA_ERR_UNSUPPORTED;
-  if (s->batch * s->q_heads * s->n_queries * (n_c + n_g) >= (int64_t(1) << 40))
+  if (!product_below({s->batch, s->q_heads, s->n_queries, n_c + n_g}, int64_t(1) << 40))
     return HGA_ERR_SHAPE;
   return HGA_OK;
 }
@@ -271,7 +281,7 @@ static int summaries_common(const void* K, int32_t dtype, const hga_kv_layout* l
   if (head_dim != 64 && head_dim != 128) return HGA_ERR_SHAPE;
   int st = check_chunking(seq_len, chunk, group);
   if (st != HGA_OK) return st;
-  if (batch * kv_heads * seq_len >= (int64_t(1) << 40)) return HGA_ERR_SHAPE;
+  if (!product_below({batch, kv_heads, seq_len}, int64_t(1) << 40)) return HGA_ERR_SHAPE;
   hga::KvLayout L;
   st = to_layout(layout, seq_len, group, &L);
   if (st != HGA_OK) return st;
@@ -286,7 +296,7 @@ static int summaries_common(const void* K, int32_t dtype, const hga_kv_layout* l
     c_begin = t_begin / chunk;
     n_chunks = (t_end + chunk - 1) / chunk - c_begin;
   }
-  if (batch * kv_heads * n_chunks >= kMaxDim) return HGA_ERR_SHAPE;
+  if (!product_below({batch, kv_heads, n_chunks}, kMaxDim)) return HGA_ERR_SHAPE;
   const hipError_t e = hga::launch_summaries(K, dtype, L, batch, kv_heads, head_dim, seq_len,
                                              chunk, group, static_cast<int>(c_begin),
                                              static_cast<int>(n_chunks), newest, chunk_mean,

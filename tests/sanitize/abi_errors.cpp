@@ -56,6 +56,13 @@ int main() {
          HGA_ERR_WORKSPACE, "route workspace");
   expect(hga_route(&s, fake, 1, ff, ff, 256, 32, -1, 64, 0.f, fi, fi, fake, nr, nullptr),
          HGA_ERR_PARAM, "route k_chunk");
+  // each size within its own bound, their products past 64 bits
+  const int64_t huge = (int64_t{1} << 31) - 1;
+  hga_shape over{huge, huge, huge, 1, huge, 128};
+  expect(hga_attend_workspace_size(&over, 32, 64, &n), HGA_ERR_SHAPE, "attend product");
+  expect(hga_route_workspace_size(&over, 256, 32, 32, 64, &n), HGA_ERR_SHAPE, "route product");
+  expect(hga_build_summaries(fake, 1, huge, huge, huge, 128, 256, 32, ff, ff, nullptr),
+         HGA_ERR_SHAPE, "build product");
   hga_shape big = s;
   big.seq_len = int64_t{1} << 21;
   expect(hga_route_workspace_size(&big, 256, 32, 32, 64, &n), HGA_ERR_UNSUPPORTED, "route big");

@@ -145,6 +145,22 @@ def test_route_rejects_before_launch():
     assert L.hga_route_workspace_size(ctypes.byref(big), 256, 32, 32, 64, ctypes.byref(n)) == UNSUPPORTED
 
 
+def test_sizes_whose_products_overflow_are_rejected():
+    """Dimensions that each pass their own bound but whose products do not fit
+    64 bits are shape errors: the checks multiply without overflowing."""
+    L = hga.lib()
+    n = ctypes.c_size_t()
+    huge = (1 << 31) - 1
+    shapes = [_shape(batch=huge, q_heads=huge, kv_heads=huge, n_queries=1, seq_len=huge),
+              _shape(batch=huge, q_heads=1 << 20, kv_heads=1 << 20, n_queries=1 << 20)]
+    for s in shapes:
+        assert L.hga_attend_workspace_size(ctypes.byref(s), 32, 64, ctypes.byref(n)) == SHAPE
+        assert L.hga_route_workspace_size(ctypes.byref(s), 256, 32, 32, 64,
+                                          ctypes.byref(n)) == SHAPE
+    assert L.hga_build_summaries(FAKE, 1, huge, huge, huge, 128, 256, 32, FAKE, FAKE,
+                                 None) == SHAPE
+
+
 def test_attend_rejects_before_launch():
     L = hga.lib()
     n = ctypes.c_size_t()
