@@ -176,14 +176,16 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-# Zero-initialised workspaces, one per (device, role), grown on demand. The
-# library leaves their zero region at zero after each call.
+# Zero-initialised workspaces, one per (device, stream, role), grown on demand.
+# The library leaves their zero region at zero after each call. Calls that
+# share a workspace must not overlap; calls on one stream never do, so a
+# workspace of its own per stream keeps calls on different streams apart.
 _ws_lock = threading.Lock()
 _ws: dict = {}
 
 
 def _workspace(device: torch.device, role: str, nbytes: int) -> torch.Tensor:
-    key = (device.index, role)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream, role)
     with _ws_lock:
         buf = _ws.get(key)
         if buf is None or buf.numel() < nbytes:

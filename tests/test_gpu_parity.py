@@ -262,6 +262,37 @@ def test_explicit_scale_every_path(path):
     check_workload(w, inp, out, scale=s)
 
 
+def test_default_workspaces_are_per_stream():
+    """Attention calls on two streams at once, each with the binding's default
+    workspace (rows split over two workgroups joined by arrival counters in the
+    workspace): each stream gets a workspace of its own, so the results equal
+    those of the same calls made one after another."""
+    log("case per-stream workspaces")
+    w = DECODE_64K.with_(B=2, T=8192, k_chunk=4, k_group=8)
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    # split rows: their partials take workspace beyond the zero region
+    assert hga.attend_workspace_bytes(shape, w.group, w.k_group) > hga.WORKSPACE_ZERO_BYTES
+    inp = generate(w)
+    out = run_hip(w, inp)
+    Q, K, V, g = out["Q"], out["K"], out["V"], out["gidx"]
+    Q2 = -Q
+    O_a, l_a = hga.attend(Q, K, V, g, w.group)
+    O_b, l_b = hga.attend(Q2, K, V, g, w.group)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    res = []
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            r1 = hga.attend(Q, K, V, g, w.group)
+        with torch.cuda.stream(s2):
+            r2 = hga.attend(Q2, K, V, g, w.group)
+        res.append((r1, r2))
+    torch.cuda.synchronize()
+    for (O1, l1), (O2, l2) in res:
+        assert torch.equal(O1, O_a) and torch.equal(l1, l_a)
+        assert torch.equal(O2, O_b) and torch.equal(l2, l_b)
+
+
 def test_kv_in_pinned_host_memory():
     log("case pinned-host-kv")
     w = DECODE_64K.with_(T=8192, k_chunk=4, k_group=8, B=2)
