@@ -469,6 +469,40 @@ def test_attend_ignores_ids_and_pages_out_of_range(nq):
     check(O2, lse2, np.where(gone, -1, gidx_np))
 
 
+@pytest.mark.parametrize("nq", [1, 160])
+def test_seq_lens_are_clamped(nq):
+    """Per-sequence lengths past T, or negative, act as T and 0 in every call:
+    summaries, routing, attention and the decode step equal those of the
+    clamped lengths bit for bit (Nq = 160 takes the MFMA route and the tile
+    attention)."""
+    log(f"case clamped seq_lens Nq={nq}")
+    w = Workload(f"clamp-nq{nq}", 3, 8, 2, 128, 2048, nq, 128, 32, 4, 8, 1e4, "bf16", 0)
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    n_c, n_g = hga.summary_counts(w.T, w.chunk, w.group)
+
+    def run(lens):
+        layout = hga.Layout(seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+        cm = torch.zeros((w.B, w.Hkv, n_c, w.D), dtype=torch.float32, device="cuda")
+        gm = torch.zeros((w.B, w.Hkv, n_g, w.D), dtype=torch.float32, device="cuda")
+        hga.build_summaries_ex(K, w.chunk, w.group, layout=layout, seq_len=w.T,
+                               chunk_mean=cm, group_mean=gm)
+        cidx, gidx = hga.route_ex(Q, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                                  layout=layout)
+        O, lse = hga.attend_ex(Q, K, V, gidx, w.group, layout=layout, seq_len=w.T)
+        cm2, gm2 = cm.clone(), gm.clone()
+        step = hga.decode_step_ex(Q, K, V, cm2, gm2, w.T, w.chunk, w.group, w.k_chunk,
+                                  w.k_group, layout=layout)
+        torch.cuda.synchronize()
+        return [cm, gm, cidx, gidx, O, lse, cm2, gm2, *step]
+
+    got = run([w.T + 500, -7, w.T - 100])
+    want = run([w.T, 0, w.T - 100])
+    for i, (x, y) in enumerate(zip(got, want)):
+        assert torch.equal(x, y), i
+    assert (want[3][1] == -1).all()     # the empty sequence routes to nothing
+
+
 def test_paged_cache_matches_ragged_dense():
     log("case paged")
     w, inp, seq_lens = _ragged_case(1)
