@@ -293,6 +293,65 @@ def test_default_workspaces_are_per_stream():
         assert torch.equal(O2, O_b) and torch.equal(l2, l_b)
 
 
+@pytest.mark.parametrize("case", ["b1-one-launch", "b16-two-launches", "noalloc", "prefill"])
+def test_decode_step_graph_replays_match_eager(case):
+    """The decode step captured in a HIP graph, as the benchmark times it, and
+    replayed several times with other calls and synchronizations in between:
+    every replay's outputs equal the eager call's. The workspace's zero region
+    is therefore back at zero after each replay; the library clears it with a
+    fill kernel, never a memset node. The allocation-free entry point (the one
+    for callers under capture) is captured the same way."""
+    log(f"case graph replays {case}")
+    w = {"b16-two-launches": SWEEP[4096], "prefill": PREFILL_TILES[0]}.get(
+        case, DECODE_64K.with_(T=8192, k_chunk=4, k_group=8))
+    inp = generate(w)
+    Q, K, V = (to_dev(x, w.dtype) for x in (inp.Q, inp.K, inp.V))
+    cm, gm = hga.build_summaries(K, w.chunk, w.group)
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    one = hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+    assert one == (case not in ("b16-two-launches", "prefill"))
+    ws = torch.zeros(hga.decode_step_workspace_bytes(shape, w.chunk, w.group, w.k_chunk,
+                                                     w.k_group), dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(Q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    gidx = torch.empty((w.B, w.Hq, w.Nq, w.k_group), dtype=torch.int32, device="cuda")
+    cidx = torch.empty((w.B, w.Hq, w.Nq, w.k_chunk + 2), dtype=torch.int32, device="cuda")
+
+    def step():
+        if case == "noalloc":
+            hga.decode_step_noalloc(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                                    chunk_idx=cidx, group_idx=gidx, out=O, lse=lse)
+        else:
+            hga.decode_step_ex(Q, K, V, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group,
+                               chunk_idx=cidx, group_idx=gidx, out=O, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (O, lse, gidx, cidx, cm, gm)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                      # once on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(4):
+        for t in (O, lse):
+            t.zero_()
+        gidx.fill_(-5)
+        cidx.fill_(-5)
+        hga.attend(Q, K, V, want[2], w.group)      # other work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((O, lse, gidx, cidx, cm, gm), want):
+            assert torch.equal(got, ref)
+    if case != "noalloc":
+        hga.workspace_check(ws)     # no bounded wait gave up
+
+
 def test_kv_in_pinned_host_memory():
     log("case pinned-host-kv")
     w = DECODE_64K.with_(T=8192, k_chunk=4, k_group=8, B=2)
