@@ -313,3 +313,16 @@ def test_package_without_library_fails_loudly(tmp_path):
                        env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libhga.so not built" in r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2, or a multi-rank launch, exits with
+    a message before touching a device."""
+    import subprocess
+    import sys
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                           capture_output=True, text=True, timeout=120,
+                           env={**os.environ, **env})
+        assert r.returncode == 2 and "one GPU only" in r.stderr
+        assert r.stdout == ""
