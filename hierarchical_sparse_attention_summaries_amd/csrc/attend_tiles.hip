@@ -85,6 +85,28 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The union's group ids (and, with `bits`, this wave's row bits of each) for
+// 64 steps at a time: lane j holds those of step base + j and a step takes
+// its own with readlane, so no step waits for an LDS read of its own. Steps
+// only ascend.
+template <bool kBits>
+struct StepWindow {
+  int base = -kWave;
+  int g = -1;
+  uint32_t bits = 0u;
+  __device__ __forceinline__ void at(const TileLds& s, int n_u, int wave, int u, int& g_u,
+                                     uint32_t& bits_u) {
+    if (u - base >= kWave) {  // uniform over the wave
+      base = u - u % kWave;
+      const int j = base + lane_id();
+      g = j < n_u ? s.list[j] : -1;
+      if constexpr (kBits) bits = g >= 0 ? s.mask[g][wave] : 0u;
+    }
+    g_u = __builtin_amdgcn_readlane(g, u - base);
+    bits_u = kBits ? __builtin_amdgcn_readlane(bits, u - base) : 0u;
+  }
+};
+
 // This thread's share of one step (zeros past the union's end or the
 // context's end), dims (t % 16) * 8 .. +7 each: K and V of step tokens
 // t / 16 + n * (threads / 16).
@@ -93,7 +115,8 @@ struct StepRegs {
 };
 
 __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s, int n_u, int b,
-                                           int kv, int step, StepRegs& r) {
+                                           int kv, int wave, int step, StepWindow<false>& win,
+                                           StepRegs& r) {
   const int t = static_cast<int>(threadIdx.x);
   const int col = (t % 16) * 8;
   // each of the step's groups as a buffer over the tokens the context holds
@@ -105,8 +128,11 @@ __device__ __forceinline__ void fetch_step(const AttendArgs& a, const TileLds& s
     const int u = step * kSG + gi;
     int64_t base = -1;
     int n_tok = 0;
-    if (u < n_u) {
-      const int t0 = __builtin_amdgcn_readfirstlane(s.list[u]) * kTG;
+    int g_u;
+    uint32_t unused;
+    win.at(s, n_u, wave, u, g_u, unused);
+    if (g_u >= 0) {
+      const int t0 = g_u * kTG;
       base = kv_offset(a.kv, b, a.Hkv, kv, a.T, kTD, t0);
       n_tok = min(kTG, a.T - t0);
     }
@@ -222,16 +248,15 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   }
 
   // One step: kSG groups of the union, staged in LDS.
+  StepWindow<true> cwin;   // the steps computed
+  StepWindow<false> fwin;  // the steps fetched (ahead of those computed)
   auto compute = [&](int step, int buf) {
     int g[kSG];
     uint32_t bits[kSG];  // the wave's 32 rows that routed each group
     uint32_t any = 0u;
 #pragma unroll
     for (int gi = 0; gi < kSG; ++gi) {
-      const int u = step * kSG + gi;
-      // uniform over the wave: read once, so the tests below branch on scalars
-      g[gi] = u < n_u ? __builtin_amdgcn_readfirstlane(s.list[u]) : -1;
-      bits[gi] = g[gi] >= 0 ? __builtin_amdgcn_readfirstlane(s.mask[g[gi]][wave]) : 0u;
+      cwin.at(s, n_u, wave, step * kSG + gi, g[gi], bits[gi]);
       any |= bits[gi];
     }
     if (any == 0u) return;  // none of the wave's rows takes these groups
@@ -339,21 +364,21 @@ __global__ __launch_bounds__(kTThreads, 2) void attend_tiles_kernel(AttendArgs a
   // a step's loads go out two computed steps before it is stashed.
   const int n_st = (n_u + kSG - 1) / kSG;
   StepRegs r0, r1;
-  fetch_step(a, s, n_u, b, kv, 0, r0);
-  fetch_step(a, s, n_u, b, kv, 1, r1);
+  fetch_step(a, s, n_u, b, kv, wave, 0, fwin, r0);
+  fetch_step(a, s, n_u, b, kv, wave, 1, fwin, r1);
   stash_step(s, 0, r0);
   lds_barrier();
-  fetch_step(a, s, n_u, b, kv, 2, r0);
+  fetch_step(a, s, n_u, b, kv, wave, 2, fwin, r0);
   for (int st = 0; st < n_st; st += 2) {
     compute(st, 0);
     stash_step(s, 1, r1);
     lds_barrier();
     if (st + 1 >= n_st) break;
-    fetch_step(a, s, n_u, b, kv, st + 3, r1);
+    fetch_step(a, s, n_u, b, kv, wave, st + 3, fwin, r1);
     compute(st + 1, 1);
     stash_step(s, 0, r0);
     lds_barrier();
-    fetch_step(a, s, n_u, b, kv, st + 4, r0);
+    fetch_step(a, s, n_u, b, kv, wave, st + 4, fwin, r0);
   }
 
   // 5. Each row's total over its 4 lanes; each lane writes 32 dims of its rows.
