@@ -86,6 +86,29 @@ KERNEL_SOURCES = {
 }
 
 
+def cache_read_rate(torch, dev, reps=50):
+    """What the Infinity Cache delivers to a plain streaming read: the summary
+    build (every key read once, small writes) over a 128 MiB bf16 key cache,
+    warm: past the 32 MB of L2, within the 256 MB cache. GB/s of keys read."""
+    import hierarchical_sparse_attention_summaries_amd as hga
+
+    K = torch.randn((1, 4, 131072, 128), device=dev).to(torch.bfloat16)
+    cm, gm = hga.build_summaries(K, 256, 32)
+    for _ in range(5):
+        hga.build_summaries(K, 256, 32, chunk_mean=cm, group_mean=gm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    e0.record()
+    for _ in range(reps):
+        hga.build_summaries(K, 256, 32, chunk_mean=cm, group_mean=gm)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    return {"kernel": "hga_summaries", "bytes_read": K.numel() * 2,
+            "read_gbs": round(K.numel() * 2 * reps / sec / 1e9, 1)}
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
@@ -559,6 +582,8 @@ def measure(w, args, primary: bool):
         # masked tiles execute, and the bytes of each tile's union, beside
         tf = tiles["alg_flops"] / (attend_us * 1e-6) / 1e12
         tf_exec = tiles["executed_flops"] / (attend_us * 1e-6) / 1e12
+        staged_gbs = tiles["bytes"] / (attend_us * 1e-6) / 1e9
+        cache = cache_read_rate(torch, dev)
         roofline_attend = {
             "kernel": "hga_attend_tiles", "bound": "mfma", "achieved": round(tf, 2),
             "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -568,7 +593,9 @@ def measure(w, args, primary: bool):
             "executed_tflops": round(tf_exec, 1),
             "executed_frac": round(tf_exec / PEAK_MFMA_BF16_TFLOPS, 4),
             "bytes_per_launch": tiles["bytes"],
-            "gbs": round(tiles["bytes"] / (attend_us * 1e-6) / 1e9, 1),
+            "gbs": round(staged_gbs, 1),
+            "infinity_cache_read": cache,
+            "gbs_over_cache_read": round(staged_gbs / cache["read_gbs"], 3),
             "tiles": tiles["tiles"], "union_groups_per_tile": tiles["union_groups_per_tile"],
             "avg_launch_us": round(attend_us, 3)}
     roofline_step = roof("decode_step", step_bytes, decode_us)
