@@ -669,10 +669,11 @@ def measure(w, args, primary: bool):
     return out
 
 
-PHASES = ["start", "scoring item done", "the row's older score words in LDS",
-          "chunk level selected (and the refreshed words in)", "group level selected, ids in LDS",
+PHASES = ["start", "scoring item done", "wave 0: the row's older chunk words in LDS",
+          "chunk level selected and every score word in", "group level selected, ids in LDS",
           "wave 0's routed K/V folded in", "every wave's routed K/V folded in",
-          "split 0: the other splits' partials in", "split 0: hand-off words zeroed, splits merged", "end of the workgroup"]
+          "split 0: the other splits' partials in", "split 0: hand-off words zeroed, splits merged",
+          "end of the workgroup", "wave 0: chunk level selected", "wave 0: group level selected"]
 
 
 def decode_phases(w, steps):

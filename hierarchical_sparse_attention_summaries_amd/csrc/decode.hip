@@ -484,14 +484,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
       return L + 1;
     }
     // chunks 1..L-1 compete; the chosen ones land in s_kept[1..k_c] directly
-    if (ra.k_c > 0)
-      rowroute::wave_select_ids<E>(
-          L - 1, ra.k_c,
-          [&](int t, int& id) {
-            id = 1 + t;
-            return s_cs[1 + t];
-          },
-          s_kept + 1, nullptr);
+    if (ra.k_c > 0) {
+      auto item = [&](int t, int& id) {
+        id = 1 + t;
+        return s_cs[1 + t];
+      };
+      // E is sized for the larger level; when the chunk level's items fit in
+      // a slot fewer, every radix step saves that slot's compares and counts
+      // (a single wave issues at most one instruction per four cycles, so
+      // the search costs what it issues)
+      bool done = false;
+      if constexpr (E > 1) {
+        if (L - 1 <= (E - 1) * kWave) {
+          rowroute::wave_select_ids<E - 1>(L - 1, ra.k_c, item, s_kept + 1, nullptr);
+          done = true;
+        }
+      }
+      if (!done) rowroute::wave_select_ids<E>(L - 1, ra.k_c, item, s_kept + 1, nullptr);
+    }
     if (lane == 0) {
       s_kept[0] = 0;
       s_kept[ra.k_c + 1] = L;
@@ -501,9 +511,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   };
 
   // The older words come from the other scoring items, the refreshed ones
-  // (chunks cf.., groups cf * gpc..) from item 0, which finishes last. Level 1
-  // needs only chunks 1..L-1, so when those are all older chunks, wave 0
-  // selects them while the other waves wait for the refreshed words.
+  // (chunks cf.., groups cf * gpc..) from the refreshing items, which finish
+  // last. Level 1 needs only chunks 1..L-1, so when those are all older
+  // chunks (the early case: every decode row), wave 0 polls the older chunk
+  // words alone (a few scoring items write them) and selects while the other
+  // waves poll the group words and the refreshed ones.
   int n1 = 0, n2 = 0, cf = 0;
   if (Tb > 0) {
     written_range(ra, Tb, n1, n2);
@@ -517,22 +529,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   const bool stale = status0 != 0;
   if (threadIdx.x == 0) s_ok = !stale;
   __syncthreads();
-  if (!stale) {
-    poll(0, cf, 0, gf, threadIdx.x, kThreads);
-    if (!early) poll(cf, n1, gf, n2, threadIdx.x, kThreads);
-  }
-  __syncthreads();
-  HGA_PHASE(2);
   int n_kept = 0;
   if (early) {
     if (wave == 0) {
-      if (!stale) n_kept = level1();
+      if (!stale) {
+        poll(0, cf, 0, 0, lane, kWave);
+        wave_lds_sync();
+        HGA_PHASE(2);
+        n_kept = level1();
+      }
+      HGA_PHASE(10);
     } else if (!stale) {
+      poll(0, 0, 0, gf, threadIdx.x - kWave, kThreads - kWave);
       poll(cf, n1, gf, n2, threadIdx.x - kWave, kThreads - kWave);
     }
     __syncthreads();
-  } else if (wave == 0 && p >= 0 && !stale) {
-    n_kept = level1();
+  } else {
+    if (!stale) {
+      poll(0, cf, 0, gf, threadIdx.x, kThreads);
+      poll(cf, n1, gf, n2, threadIdx.x, kThreads);
+    }
+    __syncthreads();
+    HGA_PHASE(2);
+    if (wave == 0 && p >= 0 && !stale) n_kept = level1();
   }
   HGA_PHASE(3);
   const bool ok = s_ok;
@@ -544,7 +563,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
     const int gpc = ra.gpc;
     // t / gpc as a multiply-high by ceil(2^32 / gpc): exact for t * gpc < 2^32
     // (here t < 4096 items, gpc <= 512), and no branch
-    const uint64_t magic = (0x100000000ull + gpc - 1) / gpc;
+    // (ceil(2^32 / gpc) from a 32-bit division: floor((2^32 - 1) / gpc) + 1 is
+    // the same number for every gpc >= 1, and a 64-bit division is a long
+    // scalar sequence on the critical path)
+    const uint64_t magic = static_cast<uint64_t>(0xFFFFFFFFu / static_cast<uint32_t>(gpc)) + 1u;
     auto cand = [&](int t) {
       const int k = static_cast<int>((static_cast<uint64_t>(t) * magic) >> 32);
       return s_kept[k] * gpc + (t - k * gpc);
@@ -562,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
             return s_gs[id];
           },
           s_ids, gout);
+      HGA_PHASE(11);
     }
     for (int t = got + lane; t < ra.k_g; t += kWave) {
       s_ids[t] = -1;
@@ -577,12 +600,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
   // Every split of the row has read the row's scores once all have counted
   // themselves in: the finishing workgroup then zeroes every word the scoring
   // wrote for the row (each one it saw arrive).
+  // (n1, n2: written_range's counts, taken before the polls)
   auto zero_row = [&]() {
-    if (Tb <= 0) return;
-    int n_chunks, n_groups;
-    written_range(ra, Tb, n_chunks, n_groups);
-    for (int t = static_cast<int>(threadIdx.x); t < n_chunks + n_groups; t += kThreads)
-      store_shared_i32(words + (t < n_chunks ? t : ra.n_c + t - n_chunks), 0);
+    for (int t = static_cast<int>(threadIdx.x); t < n1 + n2; t += kThreads)
+      store_shared_i32(words + (t < n1 ? t : ra.n_c + t - n1), 0);
   };
   attend_body<T, D, kWaves, true, decltype(zero_row), true>(aa, st.groups_per_wave, st.n_splits,
                                                            0, bid, s_ids, !ok, zero_row);
