@@ -484,24 +484,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(RouteArgs ra, AttendAr
       return L + 1;
     }
     // chunks 1..L-1 compete; the chosen ones land in s_kept[1..k_c] directly
-    if (ra.k_c > 0) {
-      auto item = [&](int t, int& id) {
-        id = 1 + t;
-        return s_cs[1 + t];
-      };
-      // E is sized for the larger level; when the chunk level's items fit in
-      // a slot fewer, every radix step saves that slot's compares and counts
-      // (a single wave issues at most one instruction per four cycles, so
-      // the search costs what it issues)
-      bool done = false;
-      if constexpr (E > 1) {
-        if (L - 1 <= (E - 1) * kWave) {
-          rowroute::wave_select_ids<E - 1>(L - 1, ra.k_c, item, s_kept + 1, nullptr);
-          done = true;
-        }
-      }
-      if (!done) rowroute::wave_select_ids<E>(L - 1, ra.k_c, item, s_kept + 1, nullptr);
-    }
+    if (ra.k_c > 0)
+      rowroute::wave_select_ids_fit<E>(
+          L - 1, ra.k_c,
+          [&](int t, int& id) {
+            id = 1 + t;
+            return s_cs[1 + t];
+          },
+          s_kept + 1, nullptr);
     if (lane == 0) {
       s_kept[0] = 0;
       s_kept[ra.k_c + 1] = L;

@@ -171,6 +171,26 @@ __device__ __forceinline__ int wave_select_ids(int n, int k, Item item, int* out
   return before;
 }
 
+// The two selections above with one key slot fewer per lane when the n items
+// fit in it (E is sized for the larger of a route's two levels): one wave
+// issues at most one instruction per four cycles, so every radix step costs
+// what it issues, and a slot fewer saves that slot's compares and counts.
+template <int E, typename ScoreOf>
+__device__ __forceinline__ int wave_select_fit(int n, int k, ScoreOf score, int* out) {
+  if constexpr (E > 1) {
+    if (n <= (E - 1) * kWave) return wave_select<E - 1>(n, k, score, out);
+  }
+  return wave_select<E>(n, k, score, out);
+}
+template <int E, typename Item>
+__device__ __forceinline__ int wave_select_ids_fit(int n, int k, Item item, int* out,
+                                                   int32_t* gout) {
+  if constexpr (E > 1) {
+    if (n <= (E - 1) * kWave) return wave_select_ids<E - 1>(n, k, item, out, gout);
+  }
+  return wave_select_ids<E>(n, k, item, out, gout);
+}
+
 constexpr int kFreshChunks = 2;   // chunks a refresh of <= C newest keys can touch
 constexpr int kFreshMaxGpc = 16;  // groups per chunk the refresh keeps in LDS
 
@@ -367,8 +387,8 @@ __device__ __forceinline__ void route_row_body(const RouteArgs& a, int bid, floa
       for (int t = lane; t < n_kept; t += kWave) s_kept[t] = t;
     } else {
       n_kept = a.k_c + 2;
-      const int got = a.k_c > 0 ? wave_select<E>(L - 1, a.k_c, [&](int t) { return s_cs[1 + t]; },
-                                                 s_pick)
+      const int got = a.k_c > 0 ? wave_select_fit<E>(L - 1, a.k_c,
+                                                     [&](int t) { return s_cs[1 + t]; }, s_pick)
                                 : 0;
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
