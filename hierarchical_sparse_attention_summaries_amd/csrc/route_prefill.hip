@@ -236,6 +236,31 @@ __host__ __device__ inline FusedLds fused_lds(int n_c, int cap, int gpc) {
 // it) stay in one or two XCDs' L2 instead of all eight.
 __host__ __device__ inline int64_t fused_tiles_per_xcd(int64_t total) { return (total + 7) / 8; }
 
+// Chunk level of one row (wave-wide): the k_c best of chunks 1..L-1 (their
+// scores cs[1..L-1], L - 1 > k_c >= 1), ids ascending into kept[1..k_c]. Every
+// lane reads a valid score (index clamped), so the reads carry no branch and
+// issue together.
+template <int EE>
+__device__ __forceinline__ void select_chunks(const float* cs, int L, int k_c, int* kept) {
+  const int lane = lane_id();
+  uint32_t key[EE];
+#pragma unroll
+  for (int e = 0; e < EE; ++e) {
+    const int u = e * kWave + lane;
+    const float s = cs[1 + min(u, L - 2)];
+    key[e] = u < L - 1 ? order_key(s) : 0u;
+  }
+  const SelMask<EE> chosen = wave_top_k<EE>(key, k_c);
+  int before = 0;
+#pragma unroll
+  for (int e = 0; e < EE; ++e) {
+    const bool ch = (chosen >> e) & 1u;
+    const uint64_t m = ballot(ch);
+    if (ch) kept[1 + before + bits_below(m)] = 1 + e * kWave + lane;
+    before += __popcll(m);
+  }
+}
+
 template <int D, int E>
 __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(RouteArgs a,
                                                                             int n_row_tiles,
@@ -369,24 +394,16 @@ __global__ __launch_bounds__(kFusedThreads) void route_prefill_fused_kernel(Rout
       } else {
         n_kept = a.k_c + 2;
         if (a.k_c > 0) {
-          // every lane reads a valid score (index clamped; L - 1 > k_c >= 1
-          // chunks compete), so the reads carry no branch and issue together
-          uint32_t key[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const int u = e * kWave + lane;
-            const float s = cs[1 + min(u, L - 2)];
-            key[e] = u < L - 1 ? order_key(s) : 0u;
+          // one key slot fewer when chunks 1..L-1 fit in it (E is sized for
+          // the group level)
+          bool done = false;
+          if constexpr (E > 1) {
+            if (L - 1 <= (E - 1) * kWave) {
+              select_chunks<E - 1>(cs, L, a.k_c, kept);
+              done = true;
+            }
           }
-          const SelMask<E> chosen = wave_top_k<E>(key, a.k_c);
-          int before = 0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const bool ch = (chosen >> e) & 1u;
-            const uint64_t m = ballot(ch);
-            if (ch) kept[1 + before + bits_below(m)] = 1 + e * kWave + lane;
-            before += __popcll(m);
-          }
+          if (!done) select_chunks<E>(cs, L, a.k_c, kept);
         }
         if (lane == 0) {
           kept[0] = 0;
