@@ -749,6 +749,11 @@ DECODE_CASES = {
     "bf16-paged-ragged": DECODE_64K.with_(B=2, T=8192, Nq=2, k_chunk=4, k_group=8, plants=2),
     "bf16-fallback-many-rows": DECODE_64K.with_(B=40, T=4096, k_chunk=2, k_group=4, plants=1),
     "qwen3-b1-t65536": DECODE_64K,
+    # one launch with both selection orders: the row at position 8191 ranks
+    # chunks while the refreshed words arrive, the row at 8192 (chunk 32, after
+    # the first refreshed chunk) waits for every word first
+    "bf16-b2-t8193-nq2-across-chunk": DECODE_64K.with_(B=2, T=8193, Nq=2, k_chunk=4, k_group=8,
+                                                       plants=2),
 }
 
 
@@ -769,6 +774,9 @@ def test_decode_step_equals_fresh_route_then_attend(case):
         lens = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
         layout = hga.Layout(seq_lens=lens, block_table=table, page_tokens=64, n_pages=n_pages)
         Kc, Vc, info = kp, vp, (seq_lens, table, 64)
+    if "across-chunk" in case:
+        assert hga.decode_step_one_launch(hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D), w.dtype,
+                                          w.chunk, w.group, w.k_chunk, w.k_group)
     cm, gm = hga.build_summaries_ex(Kc, w.chunk, w.group, layout=layout, seq_len=w.T)
     _bump_newest(w, Kc, info)
     cm_d, gm_d = cm.clone(), gm.clone()
