@@ -838,6 +838,35 @@ def test_select_over_4094_chunks(Nq):
     assert torch.equal(c_d, out["cidx"]) and torch.equal(g_d, out["gidx"])
 
 
+# The chunk level with one key slot per lane fewer than the group level: 1967
+# middle chunks (31 keys per lane) against 2008 group candidates (32 keys per
+# lane), so the chunk level ranks with 31 slots and the group level with 32,
+# through the row route, the refreshing row route and the one-launch decode step.
+NARROW_L1 = DECODE_64K.with_(name="l1-slot-fewer-c32-g8-t63000", Hq=4, Hkv=1, T=63000, chunk=32,
+                             group=8, k_chunk=500, k_group=64, plants=4)
+
+
+def test_chunk_level_one_slot_fewer():
+    w = NARROW_L1
+    log(f"case {w.name}")
+    shape = hga.Shape(w.B, w.Hq, w.Hkv, w.Nq, w.T, w.D)
+    inp = generate(w)
+    out = run_hip(w, inp)
+    check_workload(w, inp, out)
+    Q, K, V = out["Q"], out["K"], out["V"]
+    cm, gm = out["cm"].clone(), out["gm"].clone()
+    c_f, g_f = hga.route_fresh_ex(Q, K, cm, gm, w.T, w.chunk, w.group, w.k_chunk, w.k_group)
+    torch.cuda.synchronize()
+    assert torch.equal(c_f, out["cidx"]) and torch.equal(g_f, out["gidx"])
+    assert hga.decode_step_one_launch(shape, w.dtype, w.chunk, w.group, w.k_chunk, w.k_group)
+    cm2, gm2 = out["cm"].clone(), out["gm"].clone()
+    O, lse, c_d, g_d = hga.decode_step_ex(Q, K, V, cm2, gm2, w.T, w.chunk, w.group, w.k_chunk,
+                                          w.k_group, check=True)
+    torch.cuda.synchronize()
+    check_workload(w, inp, dict(cm=cm2, gm=gm2, cidx=c_d, gidx=g_d, O=O, lse=lse))
+    assert torch.equal(c_d, out["cidx"]) and torch.equal(g_d, out["gidx"])
+
+
 def test_decode_step_status_word_is_sticky_until_reset():
     """A workspace whose status word says an earlier wait gave up: the next
     one-launch decode step reads no hand-off word and poisons every row (NaN
