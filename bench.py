@@ -918,13 +918,23 @@ def stored_counters_note(kernel: str, workload: str):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo gives it: the model name (a virtual
+    machine may shorten it, e.g. to the vendor and product line), with the
+    family, model and stepping numbers and the logical CPU count beside it."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{name} ({ids}; {os.cpu_count()} logical CPUs)" if ids else name
 
 
 if __name__ == "__main__":
